@@ -1,0 +1,236 @@
+// The C ABI (include/mnb.h): argument checks on the host, launch geometry,
+// status mapping. Nothing here allocates or synchronizes.
+#include <string.h>
+
+#include <new>
+
+#include "../../include/mnb.h"
+#include "mnb_internal.h"
+
+using namespace mnb;
+
+namespace {
+
+inline hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int dtype_bytes(int dtype) { return dtype == MNB_F16 ? 2 : 4; }
+
+// Format and shape checks common to every entry point.
+int check_format(int64_t n, int64_t k, int bits, int bs, int dtype) {
+    if (bits != 4) return MNB_ERR_BITS;
+    if (bs != 32 && bs != 64) return MNB_ERR_BLOCK;
+    if (dtype != MNB_F32 && dtype != MNB_F16) return MNB_ERR_DTYPE;
+    if (n <= 0 || k <= 0 || k % bs != 0) return MNB_ERR_SHAPE;
+    if (n > MNB_MAX_ROWS || k > MNB_MAX_K) return MNB_ERR_SHAPE;
+    return MNB_OK;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MNB_OK : MNB_ERR_HIP; }
+
+// Checks for one product; fills `variant` and the problem's launch fields.
+int prepare_product(const void *x, const void *packed, const void *y, int64_t m, int64_t n, int64_t k, int bits,
+                    int bs, int dtype, Problem *out, int *kind, int *variant) {
+    if (!x || !packed || !y) return MNB_ERR_NULL;
+    int st = check_format(n, k, bits, bs, dtype);
+    if (st) return st;
+    if (m <= 0 || m > MNB_MAX_ROWS) return MNB_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(packed) || !aligned16(y)) return MNB_ERR_ALIGN;
+    Problem p = make_problem(x, packed, const_cast<void *>(y), m, n, k, bs, dtype_bytes(dtype));
+    if (dtype == MNB_F16 && m >= 2) {
+        *kind = kKindGemm;
+        *variant = gemm_variant(m);
+        gemm_tiles(p, *variant, &p.tiles_m, &p.tiles_n);
+    } else {
+        *kind = kKindGemv;
+        *variant = gemv_variant(dtype, m);
+        if (*variant == 2 && p.kg * kTileK > gemv_max_kpad(2)) *variant = 1;
+        if (p.kg * kTileK > gemv_max_kpad(*variant)) return MNB_ERR_SHAPE;
+    }
+    *out = p;
+    return MNB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mnb_abi_version(void) { return MNB_ABI_VERSION; }
+
+const char *mnb_status_string(int status) {
+    switch (status) {
+    case MNB_OK: return "ok";
+    case MNB_ERR_NULL: return "a required pointer is NULL";
+    case MNB_ERR_BITS: return "bits must be 4";
+    case MNB_ERR_BLOCK: return "block_size must be 32 or 64";
+    case MNB_ERR_SHAPE: return "invalid shape (M, N, K > 0, K a multiple of block_size, within limits)";
+    case MNB_ERR_DTYPE: return "unsupported dtype";
+    case MNB_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case MNB_ERR_HIP: return "HIP runtime error";
+    case MNB_ERR_PLAN: return "invalid grouped plan";
+    case MNB_ERR_INVALID: return "invalid argument";
+    default: return "unknown status";
+    }
+}
+
+size_t mnb_packed_bytes(int64_t N, int64_t K, int bits, int block_size, int dtype) {
+    if (check_format(N, K, bits, block_size, dtype) != MNB_OK) return 0;
+    return (size_t)make_layout(N, K, block_size, dtype_bytes(dtype)).total;
+}
+
+int mnb_quantize_rtn(const float *w, int64_t N, int64_t K, int bits, int block_size, int dtype, uint8_t *qweight,
+                     void *scales, uint8_t *zero_points, void *stream) {
+    if (!w || !qweight || !scales || !zero_points) return MNB_ERR_NULL;
+    int st = check_format(N, K, bits, block_size, dtype);
+    if (st) return st;
+    if (!aligned16(w) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zero_points)) return MNB_ERR_ALIGN;
+    return hip_status(launch_quantize_rtn(w, N, K, block_size, dtype, qweight, scales, zero_points, as_stream(stream)));
+}
+
+int mnb_pack(const uint8_t *qweight, const void *scales, const uint8_t *zero_points, int64_t N, int64_t K, int bits,
+             int block_size, int dtype, void *packed, void *stream) {
+    if (!qweight || !scales || !zero_points || !packed) return MNB_ERR_NULL;
+    int st = check_format(N, K, bits, block_size, dtype);
+    if (st) return st;
+    if (!aligned16(qweight) || !aligned16(packed)) return MNB_ERR_ALIGN;
+    const Layout L = make_layout(N, K, block_size, dtype_bytes(dtype));
+    return hip_status(launch_pack(qweight, scales, zero_points, L, dtype, static_cast<uint8_t *>(packed),
+                                  as_stream(stream)));
+}
+
+int mnb_unpack(const void *packed, int64_t N, int64_t K, int bits, int block_size, int dtype, uint8_t *q, uint8_t *zp,
+               void *stream) {
+    if (!packed || !q || !zp) return MNB_ERR_NULL;
+    int st = check_format(N, K, bits, block_size, dtype);
+    if (st) return st;
+    if (!aligned16(packed)) return MNB_ERR_ALIGN;
+    const Layout L = make_layout(N, K, block_size, dtype_bytes(dtype));
+    return hip_status(launch_unpack(static_cast<const uint8_t *>(packed), L, q, zp, as_stream(stream)));
+}
+
+int mnb_dequant(const void *packed, int64_t N, int64_t K, int bits, int block_size, int dtype, void *w, void *stream) {
+    if (!packed || !w) return MNB_ERR_NULL;
+    int st = check_format(N, K, bits, block_size, dtype);
+    if (st) return st;
+    if (!aligned16(packed) || !aligned16(w)) return MNB_ERR_ALIGN;
+    const Layout L = make_layout(N, K, block_size, dtype_bytes(dtype));
+    return hip_status(launch_dequant(static_cast<const uint8_t *>(packed), L, dtype, w, as_stream(stream)));
+}
+
+int mnb_gemm(const void *x, const void *packed, void *y, int64_t M, int64_t N, int64_t K, int bits, int block_size,
+             int dtype, void *stream) {
+    Problem p;
+    int kind = 0, variant = 0;
+    int st = prepare_product(x, packed, y, M, N, K, bits, block_size, dtype, &p, &kind, &variant);
+    if (st) return st;
+    if (kind == kKindGemm) return hip_status(launch_gemm(p, variant, as_stream(stream)));
+    return hip_status(launch_gemv(p, dtype, variant, as_stream(stream)));
+}
+
+int mnb_gemv(const void *x, const void *packed, void *y, int64_t N, int64_t K, int bits, int block_size, int dtype,
+             void *stream) {
+    return mnb_gemm(x, packed, y, 1, N, K, bits, block_size, dtype, stream);
+}
+
+size_t mnb_plan_bytes(int count) {
+    if (count < 1 || count > kMaxPlanProblems) return 0;
+    return sizeof(PlanHeader) + sizeof(Problem) * (size_t)count;
+}
+
+int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block_size, int dtype, void *plan,
+                     size_t plan_bytes) {
+    if (!problems || !plan) return MNB_ERR_NULL;
+    const size_t need = mnb_plan_bytes(count);
+    if (need == 0 || plan_bytes < need) return MNB_ERR_PLAN;
+    int st = check_format(1, block_size, bits, block_size, dtype);
+    if (st) return st;
+
+    // Classify every problem, then lay the entries out launch by launch.
+    Problem *tmp = new (std::nothrow) Problem[count];
+    int *kinds = new (std::nothrow) int[count];
+    int *variants = new (std::nothrow) int[count];
+    if (!tmp || !kinds || !variants) {
+        delete[] tmp;
+        delete[] kinds;
+        delete[] variants;
+        return MNB_ERR_INVALID;
+    }
+    for (int i = 0; i < count && st == MNB_OK; ++i) {
+        const mnb_problem &q = problems[i];
+        st = prepare_product(q.x, q.packed, q.y, q.M, q.N, q.K, bits, block_size, dtype, &tmp[i], &kinds[i],
+                             &variants[i]);
+    }
+    if (st == MNB_OK) {
+        PlanHeader *hdr = static_cast<PlanHeader *>(plan);
+        Problem *entries = reinterpret_cast<Problem *>(hdr + 1);
+        memset(hdr, 0, sizeof(PlanHeader));
+        hdr->magic = kPlanMagic;
+        hdr->version = MNB_ABI_VERSION;
+        hdr->count = count;
+        hdr->bits = bits;
+        hdr->bs = block_size;
+        hdr->dtype = dtype;
+        int out = 0;
+        // gemv variants are 0..2, gemm variants 0..6: one launch per (kind, variant)
+        for (int kind = kKindGemv; kind <= kKindGemm && st == MNB_OK; ++kind) {
+            for (int v = 0; v < 8 && st == MNB_OK; ++v) {
+                PlanLaunch L{};
+                L.kind = kind;
+                L.variant = v;
+                L.first = out;
+                int64_t wgs = 0;
+                size_t lds = 0;
+                for (int i = 0; i < count; ++i) {
+                    if (kinds[i] != kind || variants[i] != v) continue;
+                    Problem p = tmp[i];
+                    p.variant = v;
+                    p.wg_begin = wgs;
+                    const int64_t n_wg = kind == kKindGemm ? (int64_t)p.tiles_m * p.tiles_n : gemv_workgroups(p, v);
+                    if (kind == kKindGemv && gemv_lds_bytes(p, v) > lds) lds = gemv_lds_bytes(p, v);
+                    wgs += n_wg;
+                    entries[out++] = p;
+                }
+                L.count = out - L.first;
+                if (L.count == 0) continue;
+                if (wgs > 0x7FFFFFFFLL || hdr->n_launch >= kMaxPlanLaunches) {
+                    st = MNB_ERR_PLAN;
+                    break;
+                }
+                L.wgs = wgs;
+                L.lds = (int64_t)lds;
+                hdr->launches[hdr->n_launch++] = L;
+            }
+        }
+        hdr->bytes = need;
+    }
+    delete[] tmp;
+    delete[] kinds;
+    delete[] variants;
+    return st;
+}
+
+int mnb_gemm_grouped(const void *plan_host, const void *plan_device, void *stream) {
+    if (!plan_host || !plan_device) return MNB_ERR_NULL;
+    if (!aligned16(plan_device)) return MNB_ERR_ALIGN;
+    const PlanHeader *hdr = static_cast<const PlanHeader *>(plan_host);
+    if (hdr->magic != kPlanMagic || hdr->version != MNB_ABI_VERSION || hdr->count < 1 ||
+        hdr->count > kMaxPlanProblems || hdr->n_launch < 1 || hdr->n_launch > kMaxPlanLaunches ||
+        hdr->bytes != mnb_plan_bytes(hdr->count))
+        return MNB_ERR_PLAN;
+    const Problem *dev = reinterpret_cast<const Problem *>(static_cast<const PlanHeader *>(plan_device) + 1);
+    for (int i = 0; i < hdr->n_launch; ++i) {
+        const PlanLaunch &L = hdr->launches[i];
+        if (L.first < 0 || L.count < 1 || L.first + L.count > hdr->count) return MNB_ERR_PLAN;
+        hipError_t e;
+        if (L.kind == kKindGemm) {
+            e = launch_gemm_grouped(dev + L.first, L.count, L.wgs, L.variant, as_stream(stream));
+        } else {
+            e = launch_gemv_grouped(dev + L.first, L.count, L.wgs, L.variant, (size_t)L.lds, as_stream(stream));
+        }
+        if (e != hipSuccess) return MNB_ERR_HIP;
+    }
+    return MNB_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,228 @@
+// Weight-side kernels that run once per weight or only in tests: RTN
+// quantization into the canonical format, canonical -> device layout
+// (pack), and the bit-exact read-back exports (unpack, dequant).
+#include "mnb_internal.h"
+
+namespace mnb {
+
+// ---------------------------------------------------------------------------
+// RTN quantization, one thread per (row, pair of blocks) so that each thread
+// owns whole zero-point bytes. Decisions are taken in float64: the block
+// extent including zero, the scale (hi - lo) / 15 rounded once to the scale
+// dtype, zp = clamp(rint(-lo / s), 0, 15), q = clamp(rint(w / s) + zp, 0, 15).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_rtn_kernel(const float *__restrict__ w, int64_t n_rows,
+                                                           int64_t k, int bs, uint8_t *__restrict__ qweight,
+                                                           T *__restrict__ scales, uint8_t *__restrict__ zps) {
+    const int64_t nb = k / bs;
+    const int64_t npairs = (nb + 1) / 2;
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n_rows * npairs) return;
+    const int64_t n = idx / npairs;
+    const int64_t p = idx % npairs;
+    uint32_t zbyte = 0;
+    for (int e = 0; e < 2; ++e) {
+        const int64_t b = 2 * p + e;
+        if (b >= nb) break;
+        const float *src = w + n * k + b * bs;
+        double lo = 0.0, hi = 0.0;
+        for (int i = 0; i < bs; ++i) {
+            const double v = (double)src[i];
+            lo = v < lo ? v : lo;
+            hi = v > hi ? v : hi;
+        }
+        const T stored = Io<T>::round_f64((hi - lo) / 15.0);
+        const double s = (double)stored;
+        uint32_t zp = 0;
+        if (s != 0.0) {
+            const double z = __builtin_rint(-lo / s);
+            zp = (uint32_t)(z < 0.0 ? 0.0 : (z > 15.0 ? 15.0 : z));
+        }
+        uint8_t *dst = qweight + n * (k / 2) + b * bs / 2;
+        for (int i = 0; i < bs; i += 2) {
+            uint32_t c[2] = {0u, 0u};
+            if (s != 0.0) {
+                for (int t = 0; t < 2; ++t) {
+                    const double q = __builtin_rint((double)src[i + t] / s) + (double)zp;
+                    c[t] = (uint32_t)(q < 0.0 ? 0.0 : (q > 15.0 ? 15.0 : q));
+                }
+            }
+            dst[i / 2] = (uint8_t)(c[0] | (c[1] << 4));
+        }
+        scales[n * nb + b] = stored;
+        zbyte |= zp << (4 * e);
+    }
+    zps[n * ((nb + 1) / 2) + p] = (uint8_t)zbyte;
+}
+
+// ---------------------------------------------------------------------------
+// Pack: one thread per 16-byte code slot of a tile (row r, chunk j).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t *__restrict__ qweight, Layout L,
+                                                         uint8_t *__restrict__ packed) {
+    const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t tiles = L.rg * L.kg;
+    if (slot >= tiles * 64) return;
+    const int64_t tile = slot >> 6;
+    const int l = (int)(slot & 63);
+    const int r = l & 15, j = l >> 4;
+    const int64_t g = tile / L.kg, c = tile % L.kg;
+    const int64_t n = g * kTileRows + r;
+    const int64_t k0 = c * kTileK + j * kChunk;
+    uint32_t out[4] = {0u, 0u, 0u, 0u};
+    if (n < L.n && k0 < L.k) {
+        // k0 is a multiple of 32 and K a multiple of 32: the chunk is whole.
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(qweight + n * (L.k / 2) + k0 / 2);
+        for (int t = 0; t < 4; ++t) {
+            uint32_t cw;
+            __builtin_memcpy(&cw, reinterpret_cast<const uint8_t *>(src) + 4 * t, 4);
+            out[t] = to_device_word(cw);
+        }
+    }
+    uint32_t *dst = reinterpret_cast<uint32_t *>(packed + tile * kTileCodeBytes + l * 16);
+    for (int t = 0; t < 4; ++t) dst[t] = out[t];
+}
+
+// Scales and zero points: one thread per zero-point byte of a tile (two
+// entries e = 2i, 2i+1: block jb = e / 16 of rows r and r + 1).
+template <typename T>
+__global__ __launch_bounds__(256) void pack_meta_kernel(const T *__restrict__ scales,
+                                                        const uint8_t *__restrict__ zero_points, Layout L,
+                                                        uint8_t *__restrict__ packed) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int per_tile = L.nbt * kTileRows / 2;
+    const int64_t tiles = L.rg * L.kg;
+    if (idx >= tiles * per_tile) return;
+    const int64_t tile = idx / per_tile;
+    const int i = (int)(idx % per_tile);
+    const int64_t g = tile / L.kg, c = tile % L.kg;
+    const int64_t nb = L.k / L.bs;
+    const int64_t zpb = (nb + 1) / 2;
+    T *sdst = reinterpret_cast<T *>(packed + L.scales_off) + tile * L.nbt * kTileRows;
+    uint8_t *zdst = packed + L.zp_off + tile * per_tile;
+    uint32_t zbyte = 0;
+    for (int h = 0; h < 2; ++h) {
+        const int e = 2 * i + h;
+        const int jb = e / kTileRows, r = e % kTileRows;
+        const int64_t n = g * kTileRows + r;
+        const int64_t b = c * L.nbt + jb;
+        T s = (T)0.0f;
+        uint32_t z = 0;
+        if (n < L.n && b < nb) {
+            s = scales[n * nb + b];
+            z = (zero_points[n * zpb + b / 2] >> (4 * (b & 1))) & 15u;
+        }
+        sdst[e] = s;
+        zbyte |= z << (4 * h);
+    }
+    zdst[i] = (uint8_t)zbyte;
+}
+
+// ---------------------------------------------------------------------------
+// Read-back exports, one thread per code slot, through the same helpers the
+// compute kernels use (code_at / dequant_pair_f16 / dequant_f32).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void unpack_kernel(const uint8_t *__restrict__ packed, Layout L,
+                                                     uint8_t *__restrict__ q, uint8_t *__restrict__ zp) {
+    const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t tiles = L.rg * L.kg;
+    if (slot >= tiles * 64) return;
+    const int64_t tile = slot >> 6;
+    const int l = (int)(slot & 63);
+    const int r = l & 15, j = l >> 4;
+    const int64_t g = tile / L.kg, c = tile % L.kg;
+    const int64_t n = g * kTileRows + r;
+    const int64_t k0 = c * kTileK + j * kChunk;
+    if (n >= L.n || k0 >= L.k) return;
+    const uint4 v = *reinterpret_cast<const uint4 *>(packed + tile * kTileCodeBytes + l * 16);
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    for (int t = 0; t < 4; ++t)
+        for (int u = 0; u < 8; ++u) q[n * L.k + k0 + 8 * t + u] = (uint8_t)code_at(wv[t], u);
+    const int chunks_per_block = L.bs / kChunk;
+    if (j % chunks_per_block == 0) {
+        const int e = (j / chunks_per_block) * kTileRows + r;
+        const uint8_t *tz = packed + L.zp_off + tile * (L.nbt * kTileRows / 2);
+        zp[n * (L.k / L.bs) + k0 / L.bs] = (uint8_t)zp_nibble(tz, e);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ packed, Layout L,
+                                                      T *__restrict__ w) {
+    const int64_t slot = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t tiles = L.rg * L.kg;
+    if (slot >= tiles * 64) return;
+    const int64_t tile = slot >> 6;
+    const int l = (int)(slot & 63);
+    const int r = l & 15, j = l >> 4;
+    const int64_t g = tile / L.kg, c = tile % L.kg;
+    const int64_t n = g * kTileRows + r;
+    const int64_t k0 = c * kTileK + j * kChunk;
+    if (n >= L.n || k0 >= L.k) return;
+    const uint4 v = *reinterpret_cast<const uint4 *>(packed + tile * kTileCodeBytes + l * 16);
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    const int e = (j / (L.bs / kChunk)) * kTileRows + r;
+    const T s = reinterpret_cast<const T *>(packed + L.scales_off)[tile * L.nbt * kTileRows + e];
+    const uint32_t z = zp_nibble(packed + L.zp_off + tile * (L.nbt * kTileRows / 2), e);
+    T *dst = w + n * L.k + k0;
+    if constexpr (sizeof(T) == 2) {
+        const h2 zm = zp_magic(z);
+        const h2 s2 = {s, s};
+        for (int t = 0; t < 4; ++t)
+            for (int h = 0; h < 4; ++h) {
+                const h2 d = dequant_pair_f16(wv[t], h, zm, s2);
+                dst[8 * t + 2 * h] = d.x;
+                dst[8 * t + 2 * h + 1] = d.y;
+            }
+    } else {
+        for (int t = 0; t < 4; ++t)
+            for (int u = 0; u < 8; ++u) dst[8 * t + u] = dequant_f32(code_at(wv[t], u), z, s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers.
+// ---------------------------------------------------------------------------
+static inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
+
+hipError_t launch_quantize_rtn(const float *w, int64_t n, int64_t k, int bs, int dtype, uint8_t *qweight,
+                               void *scales, uint8_t *zps, hipStream_t st) {
+    const int64_t threads = n * ((k / bs + 1) / 2);
+    if (dtype == kF16)
+        quantize_rtn_kernel<_Float16><<<grid_for(threads), 256, 0, st>>>(w, n, k, bs, qweight,
+                                                                         (_Float16 *)scales, zps);
+    else
+        quantize_rtn_kernel<float><<<grid_for(threads), 256, 0, st>>>(w, n, k, bs, qweight, (float *)scales,
+                                                                      zps);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack(const uint8_t *qweight, const void *scales, const uint8_t *zps, const Layout &L,
+                       int dtype, uint8_t *packed, hipStream_t st) {
+    const int64_t tiles = L.rg * L.kg;
+    pack_codes_kernel<<<grid_for(tiles * 64), 256, 0, st>>>(qweight, L, packed);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t meta = tiles * (L.nbt * kTileRows / 2);
+    if (dtype == kF16)
+        pack_meta_kernel<_Float16><<<grid_for(meta), 256, 0, st>>>((const _Float16 *)scales, zps, L, packed);
+    else
+        pack_meta_kernel<float><<<grid_for(meta), 256, 0, st>>>((const float *)scales, zps, L, packed);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint8_t *packed, const Layout &L, uint8_t *q, uint8_t *zp, hipStream_t st) {
+    unpack_kernel<<<grid_for(L.rg * L.kg * 64), 256, 0, st>>>(packed, L, q, zp);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t *packed, const Layout &L, int dtype, void *w, hipStream_t st) {
+    if (dtype == kF16)
+        dequant_kernel<_Float16><<<grid_for(L.rg * L.kg * 64), 256, 0, st>>>(packed, L, (_Float16 *)w);
+    else
+        dequant_kernel<float><<<grid_for(L.rg * L.kg * 64), 256, 0, st>>>(packed, L, (float *)w);
+    return hipGetLastError();
+}
+
+}  // namespace mnb

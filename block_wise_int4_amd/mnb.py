@@ -1,0 +1,260 @@
+"""Python binding for libmnb.so (include/mnb.h), through ctypes.
+
+Argument marshalling only: every function here checks Python-side types,
+takes device pointers and torch's current HIP stream, and calls the C entry
+point of the same name. PyTorch only provides device memory and streams.
+The library must be built (block_wise_int4_amd.build); nothing falls back
+to another implementation when it is missing.
+"""
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmnb.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "mnb.h")
+
+MNB_F32 = 0
+MNB_F16 = 1
+_DTYPES = {torch.float32: MNB_F32, torch.float16: MNB_F16}
+_TORCH_DTYPES = {MNB_F32: torch.float32, MNB_F16: torch.float16}
+
+STATUS = {
+    0: "MNB_OK", 1: "MNB_ERR_NULL", 2: "MNB_ERR_BITS", 3: "MNB_ERR_BLOCK", 4: "MNB_ERR_SHAPE",
+    5: "MNB_ERR_DTYPE", 6: "MNB_ERR_ALIGN", 7: "MNB_ERR_HIP", 8: "MNB_ERR_PLAN", 9: "MNB_ERR_INVALID",
+}
+
+_lib = None
+
+
+class MnbError(RuntimeError):
+    def __init__(self, fn, status, message):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({message})")
+        self.status = status
+
+
+class mnb_problem(ctypes.Structure):
+    _fields_ = [("x", ctypes.c_void_p), ("packed", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+_vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+_SIGNATURES = {
+    "mnb_abi_version": (_int, []),
+    "mnb_status_string": (ctypes.c_char_p, [_int]),
+    "mnb_packed_bytes": (_sz, [_i64, _i64, _int, _int, _int]),
+    "mnb_quantize_rtn": (_int, [_vp, _i64, _i64, _int, _int, _int, _vp, _vp, _vp, _vp]),
+    "mnb_pack": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp, _vp]),
+    "mnb_unpack": (_int, [_vp, _i64, _i64, _int, _int, _int, _vp, _vp, _vp]),
+    "mnb_dequant": (_int, [_vp, _i64, _i64, _int, _int, _int, _vp, _vp]),
+    "mnb_gemv": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
+    "mnb_gemm": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp]),
+    "mnb_plan_bytes": (_sz, [_int]),
+    "mnb_plan_grouped": (_int, [ctypes.POINTER(mnb_problem), _int, _int, _int, _int, _vp, _sz]),
+    "mnb_gemm_grouped": (_int, [_vp, _vp, _vp]),
+}
+
+
+def header_functions():
+    """Names of the functions include/mnb.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mnb_[a-z0-9_]+)\s*\(", text)))
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m block_wise_int4_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MnbError(fn, status, lib().mnb_status_string(status).decode())
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def dtype_code(dtype):
+    if dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return _DTYPES[dtype]
+
+
+def mnb_abi_version():
+    return lib().mnb_abi_version()
+
+
+def mnb_status_string(status):
+    return lib().mnb_status_string(status).decode()
+
+
+def mnb_packed_bytes(N, K, block_size, dtype, bits=4):
+    return lib().mnb_packed_bytes(N, K, bits, block_size, dtype_code(dtype))
+
+
+@dataclass
+class PackedWeight:
+    """A packed weight in device memory plus the shape it was packed for."""
+    packed: torch.Tensor
+    N: int
+    K: int
+    block_size: int
+    dtype: torch.dtype
+    bits: int = 4
+
+
+def mnb_quantize_rtn(w, block_size, dtype, bits=4, out=None):
+    """RTN-quantize float32 W[N, K] on the GPU -> (qweight, scales, zero_points), canonical layout."""
+    if w.dtype != torch.float32 or w.dim() != 2:
+        raise ValueError("w must be a 2-D float32 tensor")
+    N, K = w.shape
+    nb = K // block_size if block_size else 0
+    if out is None:
+        out = (torch.empty((N, K // 2), dtype=torch.uint8, device=w.device),
+               torch.empty((N, max(nb, 1)), dtype=dtype, device=w.device),
+               torch.empty((N, max((nb + 1) // 2, 1)), dtype=torch.uint8, device=w.device))
+    q, s, z = out
+    _check("mnb_quantize_rtn", lib().mnb_quantize_rtn(
+        _dev(w, "w"), N, K, bits, block_size, dtype_code(dtype),
+        _dev(q, "qweight"), _dev(s, "scales"), _dev(z, "zero_points"), _stream(w.device)))
+    return q, s, z
+
+
+def mnb_pack(qweight, scales, zero_points, N, K, block_size, bits=4, packed=None):
+    """Canonical format -> PackedWeight (device layout of the compute kernels)."""
+    dtype = scales.dtype
+    nbytes = mnb_packed_bytes(N, K, block_size, dtype, bits)
+    if nbytes == 0:
+        # invalid format: let the library name the error (it returns before
+        # touching the GPU, so a placeholder output address is never used)
+        _check("mnb_pack", lib().mnb_pack(
+            _dev(qweight, "qweight"), _dev(scales, "scales"), _dev(zero_points, "zero_points"),
+            N, K, bits, block_size, dtype_code(dtype), ctypes.c_void_p(256), None))
+    if packed is None:
+        packed = torch.empty(nbytes, dtype=torch.uint8, device=qweight.device)
+    elif packed.numel() * packed.element_size() < nbytes:
+        raise ValueError("packed buffer too small")
+    _check("mnb_pack", lib().mnb_pack(
+        _dev(qweight, "qweight"), _dev(scales, "scales"), _dev(zero_points, "zero_points"),
+        N, K, bits, block_size, dtype_code(dtype), _dev(packed, "packed"), _stream(qweight.device)))
+    return PackedWeight(packed, N, K, block_size, dtype, bits)
+
+
+def mnb_unpack(pw):
+    """Read back (q uint8 [N, K], zp uint8 [N, K/bs]) from a PackedWeight."""
+    dev = pw.packed.device
+    q = torch.empty((pw.N, pw.K), dtype=torch.uint8, device=dev)
+    zp = torch.empty((pw.N, pw.K // pw.block_size), dtype=torch.uint8, device=dev)
+    _check("mnb_unpack", lib().mnb_unpack(
+        _dev(pw.packed, "packed"), pw.N, pw.K, pw.bits, pw.block_size, dtype_code(pw.dtype),
+        _dev(q, "q"), _dev(zp, "zp"), _stream(dev)))
+    return q, zp
+
+
+def mnb_dequant(pw):
+    """Dequantized weights [N, K] in the scale dtype."""
+    dev = pw.packed.device
+    w = torch.empty((pw.N, pw.K), dtype=pw.dtype, device=dev)
+    _check("mnb_dequant", lib().mnb_dequant(
+        _dev(pw.packed, "packed"), pw.N, pw.K, pw.bits, pw.block_size, dtype_code(pw.dtype),
+        _dev(w, "w"), _stream(dev)))
+    return w
+
+
+def _check_x(x, pw, name="x"):
+    if x.dtype != pw.dtype:
+        raise ValueError(f"{name} dtype {x.dtype} differs from the weight's {pw.dtype}")
+    if x.shape[-1] != pw.K:
+        raise ValueError(f"{name} has {x.shape[-1]} inputs, the weight {pw.K}")
+
+
+def mnb_gemv(x, pw, y=None):
+    """y[N] = x[K] @ dequant(W)^T."""
+    _check_x(x, pw)
+    if x.numel() != pw.K:
+        raise ValueError("mnb_gemv takes one activation row")
+    if y is None:
+        y = torch.empty(pw.N, dtype=pw.dtype, device=x.device)
+    _check("mnb_gemv", lib().mnb_gemv(
+        _dev(x, "x"), _dev(pw.packed, "packed"), _dev(y, "y"), pw.N, pw.K, pw.bits, pw.block_size,
+        dtype_code(pw.dtype), _stream(x.device)))
+    return y
+
+
+def mnb_gemm(x, pw, y=None):
+    """Y[M, N] = X[M, K] @ dequant(W)^T for any M >= 1."""
+    _check_x(x, pw)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, pw.N), dtype=pw.dtype, device=x.device)
+    _check("mnb_gemm", lib().mnb_gemm(
+        _dev(x, "x"), _dev(pw.packed, "packed"), _dev(y, "y"), M, pw.N, pw.K, pw.bits, pw.block_size,
+        dtype_code(pw.dtype), _stream(x.device)))
+    return y
+
+
+@dataclass
+class Plan:
+    host: torch.Tensor       # uint8 image written by mnb_plan_grouped (CPU)
+    device: torch.Tensor     # the same bytes in device memory
+    outputs: list            # the y tensors, in problem order (kept alive)
+    inputs: list             # the x tensors and packed weights (kept alive)
+
+
+def mnb_plan_grouped(problems, block_size, dtype, device=None, bits=4):
+    """problems: list of (x [M, K], PackedWeight, y [M, N] or None). Returns a Plan."""
+    count = len(problems)
+    nbytes = lib().mnb_plan_bytes(count)
+    if nbytes == 0:
+        raise MnbError("mnb_plan_bytes", 8, "count out of range")
+    arr = (mnb_problem * count)()
+    outs, keep = [], []
+    for i, (x, pw, y) in enumerate(problems):
+        _check_x(x, pw)
+        M = 1 if x.dim() == 1 else x.shape[0]
+        if y is None:
+            y = torch.empty((M, pw.N), dtype=pw.dtype, device=x.device)
+        arr[i] = mnb_problem(_dev(x, "x").value, _dev(pw.packed, "packed").value, _dev(y, "y").value,
+                             M, pw.N, pw.K)
+        outs.append(y)
+        keep.append((x, pw))
+    host = torch.empty(nbytes, dtype=torch.uint8)
+    _check("mnb_plan_grouped", lib().mnb_plan_grouped(arr, count, bits, block_size, dtype_code(dtype),
+                                                      ctypes.c_void_p(host.data_ptr()), nbytes))
+    dev = host.to(device or problems[0][0].device)
+    return Plan(host, dev, outs, keep)
+
+
+def mnb_gemm_grouped(plan):
+    """Run every product of a plan (one launch per kernel class present)."""
+    _check("mnb_gemm_grouped", lib().mnb_gemm_grouped(
+        ctypes.c_void_p(plan.host.data_ptr()), _dev(plan.device, "plan_device"), _stream(plan.device.device)))
+    return plan.outputs

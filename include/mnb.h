@@ -1,0 +1,187 @@
+/*
+ * mnb.h - MatMulNBits for AMD Instinct MI355X (gfx950): weight-only,
+ * block-wise, asymmetric 4-bit quantized matrix multiplication.
+ *
+ *   Y[M, N] = X[M, K] * D[N, K]^T,   D[n, k] = (q[n, k] - zp[n, b]) * s[n, b],
+ *   b = k / block_size.
+ *
+ * The operator is the one the int4 ONNX model cards call MatMulNBits:
+ * 4-bit codes, blocks of 32 inputs, asymmetric ("Mega-ASR INT4 ONNX",
+ * section "Conversion details"); round-to-nearest, block 32, fp16 float
+ * tensors in the q4f16 variant ("Qwen3-ASR-0.6B ONNX for the browser",
+ * section "Pick a variant" and section "Graph contracts"); block 64
+ * ("sherpa-onnx STT int4", section "whisper-small"; "qwen3-asr-0.6b-onnx-
+ * int4-merged", section "Provenance"); only the weights are quantized and
+ * activations enter as they are ("sherpa-onnx STT int4", section "Why int4
+ * rather than the usual int8").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers named x, y, w, qweight, scales, zero_points, packed, q, zp are
+ *    DEVICE pointers. The caller owns all memory; the library allocates,
+ *    frees and synchronizes nothing, and keeps no mutable global state, so
+ *    calls are reentrant. Calls on one stream run in order.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call that touches device memory is asynchronous on it.
+ *  - bits must be 4, block_size 32 or 64, K a positive multiple of
+ *    block_size, M and N positive.
+ *  - dtype is the activation dtype, which is also the scale dtype and the
+ *    output dtype: MNB_F32 or MNB_F16. Accumulation is float32.
+ *  - Every argument is checked on the host before anything is enqueued; on
+ *    error nothing is enqueued and a nonzero mnb_status is returned. A launch
+ *    failure reported by the HIP runtime returns MNB_ERR_HIP.
+ *  - Device pointers must be 16-byte aligned (MNB_ERR_ALIGN otherwise);
+ *    outputs must not overlap inputs.
+ *  - The packed buffer carries no header: pack and use must be given the
+ *    same (N, K, block_size, dtype). This is documented, not checked.
+ *
+ * Canonical (interchange) weight format, as produced by mnb_quantize_rtn and
+ * consumed by mnb_pack:
+ *  - qweight     uint8 [N][K/2]: byte j of row n holds code k = 2j in bits
+ *                0-3 and k = 2j+1 in bits 4-7 (low nibble first).
+ *  - scales      dtype [N][K/block_size].
+ *  - zero_points uint8 [N][ceil(K/block_size/2)]: byte i of row n holds the
+ *                zero point of block 2i in bits 0-3 and of block 2i+1 in bits
+ *                4-7; an odd block count leaves a zero pad nibble.
+ */
+#ifndef MNB_H
+#define MNB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MNB_ABI_VERSION 1
+
+typedef enum mnb_dtype {
+    MNB_F32 = 0, /* float32 activations, scales and outputs */
+    MNB_F16 = 1  /* float16 activations, scales and outputs */
+} mnb_dtype;
+
+typedef enum mnb_status {
+    MNB_OK = 0,
+    MNB_ERR_NULL = 1,      /* a required pointer is NULL                     */
+    MNB_ERR_BITS = 2,      /* bits != 4                                      */
+    MNB_ERR_BLOCK = 3,     /* block_size not 32 or 64                        */
+    MNB_ERR_SHAPE = 4,     /* M, N, K <= 0, K % block_size != 0, or a size
+                              beyond the documented limits                    */
+    MNB_ERR_DTYPE = 5,     /* dtype not MNB_F32 / MNB_F16, or not supported
+                              by this entry point                             */
+    MNB_ERR_ALIGN = 6,     /* a device pointer is not 16-byte aligned        */
+    MNB_ERR_HIP = 7,       /* the HIP runtime reported a launch error        */
+    MNB_ERR_PLAN = 8,      /* grouped plan: bad count, size or contents      */
+    MNB_ERR_INVALID = 9    /* any other invalid argument                     */
+} mnb_status;
+
+/* Limits checked by the entry points (MNB_ERR_SHAPE beyond them). */
+#define MNB_MAX_K 32768            /* inputs per row                         */
+#define MNB_MAX_ROWS 0x7FFFFFF0LL  /* M and N                                */
+
+/* ABI version of the loaded library (MNB_ABI_VERSION it was built with). */
+int mnb_abi_version(void);
+
+/* Static description of a status code; never NULL, "unknown status" for
+ * values outside the enum. */
+const char *mnb_status_string(int status);
+
+/* Bytes of device memory mnb_pack writes for one weight, or 0 if the
+ * arguments are invalid. Host only. Padding rounds N up to 16 and K up to
+ * 128 and is filled with zero codes, zero scales and zero zero-points. */
+size_t mnb_packed_bytes(int64_t N, int64_t K, int bits, int block_size, int dtype);
+
+/*
+ * Round-to-nearest block quantization of a float32 weight W[N][K] into the
+ * canonical format. The pages name the quantizer (RTN, blocks along K,
+ * asymmetric; "Qwen3-ASR-0.6B ONNX for the browser", section "Pick a
+ * variant"; "Mega-ASR INT4 ONNX", section "Conversion details") but print no
+ * formula; per block this computes, in float64:
+ *   lo = min(0, min w), hi = max(0, max w),
+ *   s  = (hi - lo) / 15 rounded once (half to even) to dtype,
+ *   zp = clamp(rint(-lo / s), 0, 15), q = clamp(rint(w / s) + zp, 0, 15),
+ * and zp = q = 0 for a block whose stored scale is 0. rint rounds half to
+ * even. w: device float32 [N][K]. Outputs: qweight [N][K/2], scales
+ * [N][K/bs] of dtype, zero_points [N][ceil(K/bs/2)] (canonical layout).
+ * Weights must be finite. Not a hot-path call (offline tooling).
+ */
+int mnb_quantize_rtn(const float *w, int64_t N, int64_t K, int bits, int block_size, int dtype,
+                     uint8_t *qweight, void *scales, uint8_t *zero_points, void *stream);
+
+/*
+ * Canonical format -> the device layout the compute kernels read, written to
+ * `packed` (mnb_packed_bytes(...) bytes, device). Runs once per weight.
+ */
+int mnb_pack(const uint8_t *qweight, const void *scales, const uint8_t *zero_points,
+             int64_t N, int64_t K, int bits, int block_size, int dtype,
+             void *packed, void *stream);
+
+/*
+ * Test export: the unpacked codes q uint8 [N][K] (values 0..15) and zero
+ * points zp uint8 [N][K/bs], read back from `packed` with the same device
+ * functions the compute kernels use. Bit-exact with the canonical input.
+ */
+int mnb_unpack(const void *packed, int64_t N, int64_t K, int bits, int block_size, int dtype,
+               uint8_t *q, uint8_t *zp, void *stream);
+
+/*
+ * Test export: dequantized weights w [N][K] in dtype, each (q - zp) formed
+ * exactly and multiplied by s with one round-half-to-even rounding, using
+ * the same device functions as the GEMM's weight tiles. Bit-exact.
+ */
+int mnb_dequant(const void *packed, int64_t N, int64_t K, int bits, int block_size, int dtype,
+                void *w, void *stream);
+
+/*
+ * Decode-step product, M = 1: y[N] = x[K] * D^T. x and y are dtype.
+ * Accumulates in float32 and rounds y once to dtype.
+ */
+int mnb_gemv(const void *x, const void *packed, void *y,
+             int64_t N, int64_t K, int bits, int block_size, int dtype, void *stream);
+
+/*
+ * General product for any M >= 1: Y[M][N] = X[M][K] * D^T, X and Y
+ * row-major in dtype. M = 1 runs the decode kernel; float16 with M >= 2
+ * runs the matrix-core (MFMA) kernel that dequantizes weight tiles and feeds
+ * fp16 MFMA with float32 accumulation; float32 with M >= 2 runs a vector
+ * kernel.
+ */
+int mnb_gemm(const void *x, const void *packed, void *y,
+             int64_t M, int64_t N, int64_t K, int bits, int block_size, int dtype, void *stream);
+
+/*
+ * Grouped execution: many independent products in one launch per kernel
+ * class (one for the M = 1 problems, one for the M >= 2 problems). All
+ * problems of a plan share bits, block_size and dtype.
+ */
+typedef struct mnb_problem {
+    const void *x;      /* device, [M][K] dtype                          */
+    const void *packed; /* device, mnb_pack output for (N, K)            */
+    void *y;            /* device, [M][N] dtype                          */
+    int64_t M, N, K;
+} mnb_problem;
+
+/* Bytes of a plan for `count` problems (0 if count is out of range 1..65536). */
+size_t mnb_plan_bytes(int count);
+
+/*
+ * Host only: validate `problems[0..count)` and write a plan (a position-
+ * independent byte image of mnb_plan_bytes(count) bytes) into the HOST
+ * buffer `plan`. The caller copies that image to device memory unchanged.
+ */
+int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block_size, int dtype,
+                     void *plan, size_t plan_bytes);
+
+/*
+ * Run a plan. plan_host: the host image written by mnb_plan_grouped (read
+ * for launch geometry); plan_device: a device copy of the same bytes (read
+ * by the kernels). The two must be identical; the host copy is re-checked.
+ */
+int mnb_gemm_grouped(const void *plan_host, const void *plan_device, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MNB_H */

@@ -1,0 +1,212 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact: RTN codes, scales and zero points; unpacked codes; dequantized
+weights. Within tolerance (max |y - y_ref| <= tol * max |y_ref| per call):
+outputs, tol = 2e-3 for float16 activations and 1e-5 for float32.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_wise_int4_amd import mnb
+from workloads import configs, synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = {np.float16: 2e-3, np.float32: 1e-5}
+NP = {torch.float16: np.float16, torch.float32: np.float32}
+TD = {np.float16: torch.float16, np.float32: torch.float32}
+
+
+def special_weight(n, k, bs, seed):
+    """N(0, 0.02) rows with edge blocks planted: all zero, single-signed
+    (both signs), an exact RNE tie for the zero point, a tiny block whose
+    float16 scale underflows, and a wide-range block."""
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    nb = k // bs
+    if n >= 6 and nb >= 1:
+        w[0, :bs] = 0.0
+        w[1, :bs] = np.abs(w[1, :bs]) + 0.001
+        w[2, :bs] = -np.abs(w[2, :bs]) - 0.001
+        sc = 2.0 ** -7
+        t = np.zeros(bs)
+        t[:4] = np.array([-2.5, 12.5, 0.5, 1.5]) * sc
+        w[3, :bs] = t
+        w[4, :bs] = rng.standard_normal(bs) * 1e-9
+        w[5, :bs] = rng.standard_normal(bs) * 30.0
+    return w
+
+
+def quantize_oracle(w, bs, dt):
+    q, s, zp = oracle.rtn_quantize(w, bs, dt)
+    qw, pz = oracle.pack_weight(q, zp)
+    return q, s, zp, qw, pz
+
+
+def upload_packed(qw, s, pz, n, k, bs):
+    return mnb.mnb_pack(torch.from_numpy(qw).to(DEV), torch.from_numpy(s).to(DEV),
+                        torch.from_numpy(pz).to(DEV), n, k, bs)
+
+
+SHAPES = [(64, 256, 32), (17, 96, 32), (33, 192, 64), (6, 64, 64), (40, 4160, 32), (1, 32, 32)]
+
+
+@pytest.mark.parametrize("dt", [np.float16, np.float32])
+@pytest.mark.parametrize("n,k,bs", SHAPES)
+def test_quantize_rtn_bit_exact(n, k, bs, dt):
+    w = special_weight(n, k, bs, seed=n * 31 + k)
+    q, s, zp, qw, pz = quantize_oracle(w, bs, dt)
+    gq, gs, gz = mnb.mnb_quantize_rtn(torch.from_numpy(w).to(DEV), bs, TD[dt])
+    torch.cuda.synchronize()
+    assert np.array_equal(gq.cpu().numpy(), qw)
+    assert np.array_equal(gs.cpu().numpy().view(np.uint8), s.view(np.uint8))
+    assert np.array_equal(gz.cpu().numpy(), pz)
+
+
+@pytest.mark.parametrize("dt", [np.float16, np.float32])
+@pytest.mark.parametrize("n,k,bs", SHAPES)
+def test_unpack_and_dequant_bit_exact(n, k, bs, dt):
+    w = special_weight(n, k, bs, seed=n + 7 * k)
+    q, s, zp, qw, pz = quantize_oracle(w, bs, dt)
+    pw = upload_packed(qw, s, pz, n, k, bs)
+    gq, gz = mnb.mnb_unpack(pw)
+    d = mnb.mnb_dequant(pw)
+    torch.cuda.synchronize()
+    assert np.array_equal(gq.cpu().numpy(), q)
+    assert np.array_equal(gz.cpu().numpy(), zp)
+    ref = oracle.dequantize(q, zp, s, bs, dt)
+    assert np.array_equal(d.cpu().numpy().view(np.uint8), ref.view(np.uint8))
+
+
+def run_product(m, n, k, bs, dt, seed, std=0.02):
+    w, x = synth.random_case(seed, m, n, k, "f16" if dt == np.float16 else "f32", std)
+    q, s, zp, qw, pz = quantize_oracle(w, bs, dt)
+    pw = upload_packed(qw, s, pz, n, k, bs)
+    xd = torch.from_numpy(x).to(DEV)
+    y = mnb.mnb_gemv(xd.reshape(-1), pw) if m == 1 else mnb.mnb_gemm(xd, pw)
+    torch.cuda.synchronize()
+    ref = oracle.matmul_nbits(x, q, zp, s, bs)
+    return y.cpu().numpy().reshape(m, n), ref
+
+
+GEMV_CASES = [(3072, 1024, 32, np.float32), (1, 32, 32, np.float16), (17, 96, 32, np.float16),
+              (100, 192, 64, np.float16), (64, 2048, 32, np.float16), (300, 4160, 32, np.float16),
+              (33, 8192, 32, np.float32), (2048, 1024, 32, np.float16), (5, 32768, 32, np.float16),
+              (250, 736, 32, np.float32), (96, 768, 64, np.float32)]
+
+
+@pytest.mark.parametrize("n,k,bs,dt", GEMV_CASES)
+def test_gemv_parity(n, k, bs, dt):
+    y, ref = run_product(1, n, k, bs, dt, seed=n + k)
+    ok, err, mx = oracle.within_tolerance(y, ref, TOL[dt])
+    assert ok, f"max err {err:.3e} vs {TOL[dt]} * {mx:.3e}"
+
+
+GEMM_CASES = [(2, 64, 64, 32), (7, 200, 256, 32), (16, 1024, 2048, 32), (17, 96, 96, 32), (31, 130, 512, 64),
+              (33, 64, 1024, 32), (64, 300, 4160, 32), (65, 512, 768, 64), (100, 256, 2048, 32),
+              (130, 1024, 768, 64), (257, 384, 1024, 32), (410, 1024, 2048, 32), (500, 200, 3072, 64),
+              (1500, 768, 768, 64)]
+
+
+@pytest.mark.parametrize("m,n,k,bs", GEMM_CASES)
+def test_gemm_fp16_parity(m, n, k, bs):
+    y, ref = run_product(m, n, k, bs, np.float16, seed=m * 1000 + n + k)
+    ok, err, mx = oracle.within_tolerance(y, ref, TOL[np.float16])
+    assert ok, f"max err {err:.3e} vs 2e-3 * {mx:.3e}"
+
+
+@pytest.mark.parametrize("m,n,k,bs", [(2, 64, 1024, 32), (5, 100, 4096, 32), (3, 40, 8192, 64), (9, 17, 96, 32)])
+def test_gemm_fp32_parity(m, n, k, bs):
+    y, ref = run_product(m, n, k, bs, np.float32, seed=m + n + k)
+    ok, err, mx = oracle.within_tolerance(y, ref, TOL[np.float32])
+    assert ok, f"max err {err:.3e} vs 1e-5 * {mx:.3e}"
+
+
+def test_grouped_plan_matches_single_calls_bitwise():
+    specs = [(1, 256, 1024, 1), (1, 17, 96, 2), (410, 128, 256, 3), (33, 64, 512, 4), (1, 2048, 2048, 5),
+             (1500, 64, 768, 6)]
+    problems, singles, refs = [], [], []
+    for m, n, k, seed in specs:
+        w, x = synth.random_case(seed, m, n, k, "f16")
+        q, s, zp, qw, pz = quantize_oracle(w, 32, np.float16)
+        pw = upload_packed(qw, s, pz, n, k, 32)
+        xd = torch.from_numpy(x).to(DEV)
+        problems.append((xd, pw, None))
+        singles.append(mnb.mnb_gemm(xd, pw))
+        refs.append((x, q, zp, s))
+    plan = mnb.mnb_plan_grouped(problems, 32, torch.float16)
+    outs = mnb.mnb_gemm_grouped(plan)
+    torch.cuda.synchronize()
+    for y, ys, (x, q, zp, s) in zip(outs, singles, refs):
+        assert torch.equal(y, ys)
+        ok, err, mx = oracle.within_tolerance(y.cpu().numpy(), oracle.matmul_nbits(x, q, zp, s, 32), 2e-3)
+        assert ok, (err, mx)
+
+
+def test_repeated_calls_are_deterministic():
+    w, x = synth.random_case(3, 410, 512, 2048, "f16")
+    q, s, zp, qw, pz = quantize_oracle(w, 32, np.float16)
+    pw = upload_packed(qw, s, pz, 512, 2048, 32)
+    xd = torch.from_numpy(x).to(DEV)
+    a = mnb.mnb_gemm(xd, pw)
+    b = mnb.mnb_gemm(xd, pw)
+    g1 = mnb.mnb_gemv(xd[0].contiguous(), pw)
+    g2 = mnb.mnb_gemv(xd[0].contiguous(), pw)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(g1, g2)
+
+
+def test_errors_raise_and_enqueue_nothing():
+    w, x = synth.random_case(1, 4, 64, 128, "f16")
+    q, s, zp, qw, pz = quantize_oracle(w, 32, np.float16)
+    pw = upload_packed(qw, s, pz, 64, 128, 32)
+    y = torch.full((64,), 7.0, dtype=torch.float16, device=DEV)
+    bad = mnb.PackedWeight(pw.packed, 64, 96, 64, torch.float16)        # K % bs != 0
+    with pytest.raises(mnb.MnbError) as ei:
+        mnb.mnb_gemv(torch.zeros(96, dtype=torch.float16, device=DEV), bad, y)
+    assert ei.value.status == 4
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+# ---------------------------------------------------------------------------
+# Full-size configurations, in the launch configuration the benchmark times
+# (one grouped plan over the config's linears), checked on sampled rows.
+# ---------------------------------------------------------------------------
+
+def _full_size_subset(cfg):
+    if cfg.index == 0:
+        return list(cfg.linears)
+    layer0 = [l for l in cfg.linears if l.layer == 0]
+    last = [l for l in cfg.linears if l.layer == max(x.layer for x in cfg.linears)]
+    return layer0 + last
+
+
+@pytest.mark.parametrize("ci", [0, 1, 2, 3, 4])
+def test_full_size_config_sampled(ci):
+    from block_wise_int4_amd import workload
+    cfg = configs.CONFIGS[ci]
+    lins = _full_size_subset(cfg)
+    print(f"config {cfg.name}: {len(lins)} linears", flush=True)
+    data = workload.build_config(cfg, DEV, linears=lins, sample_rows=12)
+    plan = workload.make_plan(cfg, data.linears)
+    mnb.mnb_gemm_grouped(plan)
+    torch.cuda.synchronize()
+    dt = np.float16 if cfg.dtype == "f16" else np.float32
+    for ld in data.linears:
+        rows = ld.sample_rows
+        q, s, zp = oracle.rtn_quantize(ld.w_rows, cfg.block_size, dt)
+        gq, gs, gz = ld.canonical
+        qw, pz = oracle.pack_weight(q, zp)
+        assert np.array_equal(gq, qw) and np.array_equal(gz, pz)
+        assert np.array_equal(gs.view(np.uint8), s.view(np.uint8))
+        x = ld.x.cpu().numpy()
+        mrows = np.unique(np.linspace(0, cfg.m - 1, min(cfg.m, 6)).astype(int))
+        ref = oracle.matmul_nbits(x[mrows], q, zp, s, cfg.block_size)
+        got = ld.y.cpu().numpy()[np.ix_(mrows, rows)]
+        ok, err, mx = oracle.within_tolerance(got, ref, TOL[dt])
+        assert ok, f"{ld.lin}: err {err:.3e} vs {TOL[dt]} * {mx:.3e}"
