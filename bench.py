@@ -1,0 +1,263 @@
+"""MatMulNBits benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--prefill-config 3]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+every linear of the workload (read activations, stream the packed int4
+codes, scales and zero points, unpack, dequantize, contract, write outputs),
+issued as one grouped launch. The headline workload is the Qwen3-0.6B-shaped
+decode step (197 GEMVs: 28 layers x 7 projections + the LM head, M = 1,
+block 32, fp16 activations). The same run also times the Qwen3-1.7B-shaped
+prefill (196 GEMMs at M = 410) for the TFLOP/s half of the metric.
+
+Inputs are resident in HBM before timing starts; the step rotates over
+enough replicas of the weights to exceed the 256 MB last-level cache. Times
+come from HIP events on the stream the kernels run on, over exactly K steps
+bracketed by device synchronizations. Rank 0 prints one JSON line.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
+LLC_BYTES = 256e6              # Infinity Cache
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ("mnb_gemv.hip", "mnb_gemm.hip", "mnb_device.h", "mnb_layout.h", "mnb_internal.h")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_wise_int4_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel_key):
+    """HBM bytes per launch measured with rocprofv3 counters for this kernel
+    source, or None if absent or taken on a different source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != kernel_source_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_steps(fn_list, steps, warmup, torch):
+    """Run fn_list[i % R]() for warmup + steps; time the last `steps` with
+    events on the current stream. Returns ms per step."""
+    R = len(fn_list)
+    for i in range(warmup):
+        fn_list[i % R]()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn_list[(warmup + i) % R]()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def run_workload(cfg, steps, warmup, per_linear, torch, dev):
+    from block_wise_int4_amd import mnb, workload
+
+    t0 = time.time()
+    log(f"[bench] {cfg.name}: quantizing and packing {len(cfg.linears)} linears on the GPU")
+    base = workload.build_config(cfg, dev).linears
+    algo = workload.algorithmic_bytes(cfg)
+    flops = workload.flops(cfg)
+    weight_bytes = sum(ld.pw.packed.numel() for ld in base)
+    io_bytes = sum(ld.x.numel() * ld.x.element_size() + ld.y.numel() * ld.y.element_size() for ld in base)
+    replicas = max(1, math.ceil(1.1e9 / (weight_bytes + io_bytes)))
+    sets = [base] + [workload.replicate(cfg, base) for _ in range(replicas - 1)]
+    plans = [workload.make_plan(cfg, s) for s in sets]
+    torch.cuda.synchronize()
+    log(f"[bench] {cfg.name}: ready in {time.time() - t0:.1f}s, {replicas} replicas "
+        f"({replicas * (weight_bytes + io_bytes) / 1e9:.2f} GB resident)")
+
+    ms = time_steps([lambda p=p: mnb.mnb_gemm_grouped(p) for p in plans], steps, warmup, torch)
+    log(f"[bench] {cfg.name}: grouped {ms * 1e3:.1f} us/step")
+    out = {"ms": ms, "bytes": algo, "flops": flops, "replicas": replicas,
+           "launches_per_step": mnb.mnb_plan_launches(plans[0])}
+    if per_linear:
+        def one_pass(s):
+            def f():
+                for ld in s:
+                    if cfg.m == 1:
+                        mnb.mnb_gemv(ld.x.reshape(-1), ld.pw, ld.y.reshape(-1))
+                    else:
+                        mnb.mnb_gemm(ld.x, ld.pw, ld.y)
+            return f
+        pl_steps = max(3, steps // 4)
+        out["per_linear_ms"] = time_steps([one_pass(s) for s in sets], pl_steps, min(warmup, 3), torch)
+        log(f"[bench] {cfg.name}: per-linear {out['per_linear_ms'] * 1e3:.1f} us/step")
+    del plans, sets, base
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(cfg, budget_s):
+    """The oracle (NumPy float64 dequantize + matmul) on the host cores, on a
+    bounded prefix of the workload's linears. Quantization is not timed."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from workloads import synth
+
+    dt = np.float16 if cfg.dtype == "f16" else np.float32
+    done_bytes, done_flops, elapsed, used = 0, 0, 0.0, []
+    for lin in cfg.linears:
+        if elapsed >= budget_s:
+            break
+        w, x = synth.linear_inputs(cfg, lin)
+        n_rows = lin.n
+        if lin.proj == "lm_head":
+            n_rows = min(lin.n, 16384)   # a slice of the vocabulary keeps the sample bounded
+            w = w[:n_rows]
+        q, s, zp = oracle.rtn_quantize(w, cfg.block_size, dt)
+        t = time.perf_counter()
+        oracle.matmul_nbits(x, q, zp, s, cfg.block_size)
+        elapsed += time.perf_counter() - t
+        nb = lin.k // cfg.block_size
+        a = 2 if cfg.dtype == "f16" else 4
+        done_bytes += n_rows * lin.k // 2 + n_rows * nb * a + n_rows * ((nb + 1) // 2) + cfg.m * (lin.k + n_rows) * a
+        done_flops += 2 * cfg.m * n_rows * lin.k
+        used.append(f"{lin.proj}{'' if lin.layer < 0 else lin.layer}" + ("" if n_rows == lin.n else f"[:{n_rows}]"))
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"seconds": elapsed, "bytes": done_bytes, "flops": done_flops, "threads": threads,
+            "sample": f"{len(used)} of {len(cfg.linears)} linears in order ({used[0]}..{used[-1]}), "
+                      f"{done_bytes / 1e6:.1f} MB algorithmic"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=1, help="headline workload (index into workloads.configs)")
+    ap.add_argument("--prefill-config", type=int, default=3, help="prefill workload timed alongside; -1 = none")
+    ap.add_argument("--no-per-linear", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per workload")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this size (counter calibration runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_wise_int4_amd import mnb
+    from workloads import configs
+
+    if not os.path.exists(mnb.LIB_PATH):
+        from block_wise_int4_amd import build as _b
+        _b.build()
+    mnb.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {n} bytes read, {n} bytes written")
+        del a, b
+
+    cfg = configs.CONFIGS[args.config]
+    dec = run_workload(cfg, args.steps, args.warmup, not args.no_per_linear, torch, dev)
+    gbs = dec["bytes"] / (dec["ms"] * 1e-3) / 1e9
+    decode_kernel = "gemv_grouped_f16" if cfg.m == 1 else "gemm_grouped"
+    dec_traffic = stored_traffic(f"{decode_kernel}:{cfg.name}")
+
+    result = {
+        "metric": "int4 MatMulNBits decode GB/s (M=1) & prefill TFLOP/s, % of MI355X roofline",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,0.02) weights RTN-quantized on the GPU, N(0,1) activations)",
+        "config": {
+            "workload": cfg.name, "M": cfg.m, "linears": len(cfg.linears), "block_size": cfg.block_size,
+            "activations": cfg.dtype, "accumulate": "f32", "schedule": "grouped",
+            "launches_per_step": dec["launches_per_step"], "replicas": dec["replicas"],
+            "algorithmic_bytes_per_step": dec["bytes"],
+            "per_linear_ms_per_step": round(dec.get("per_linear_ms", float("nan")), 5),
+            "per_linear_GBps": round(dec["bytes"] / (dec["per_linear_ms"] * 1e-3) / 1e9, 2)
+            if "per_linear_ms" in dec else None,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": dec_traffic,
+        },
+    }
+
+    if args.prefill_config >= 0:
+        pcfg = configs.CONFIGS[args.prefill_config]
+        pre = run_workload(pcfg, max(5, args.steps // 2), max(2, args.warmup // 2), not args.no_per_linear,
+                           torch, dev)
+        tf = pre["flops"] / (pre["ms"] * 1e-3) / 1e12
+        result["prefill"] = {
+            "workload": pcfg.name, "M": pcfg.m, "linears": len(pcfg.linears), "value": round(tf, 2),
+            "unit": "TFLOP/s", "ms_per_step": round(pre["ms"], 5), "schedule": "grouped",
+            "launches_per_step": pre["launches_per_step"],
+            "per_linear_TFLOPs": round(pre["flops"] / (pre["per_linear_ms"] * 1e-3) / 1e12, 2)
+            if "per_linear_ms" in pre else None,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                         "traffic": stored_traffic(f"gemm_grouped:{pcfg.name}")},
+        }
+
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline: oracle on {cfg.name} (budget {args.cpu_budget:.0f}s)")
+        cb = cpu_baseline(cfg, args.cpu_budget)
+        result["cpu_baseline"] = {
+            "value": round(cb["bytes"] / cb["seconds"] / 1e9, 4), "unit": "GB/s",
+            "cores": cb["threads"], "kind": "oracle", "sample": cb["sample"],
+        }
+        if args.prefill_config >= 0:
+            pcfg = configs.CONFIGS[args.prefill_config]
+            log(f"[bench] cpu baseline: oracle on {pcfg.name}")
+            pb = cpu_baseline(pcfg, args.cpu_budget)
+            result["prefill"]["cpu_baseline"] = {
+                "value": round(pb["flops"] / pb["seconds"] / 1e12, 5), "unit": "TFLOP/s",
+                "cores": pb["threads"], "kind": "oracle", "sample": pb["sample"],
+            }
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

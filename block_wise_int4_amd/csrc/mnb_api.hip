@@ -210,6 +210,15 @@ int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block
     return st;
 }
 
+int mnb_plan_launches(const void *plan_host) {
+    if (!plan_host) return -1;
+    const PlanHeader *hdr = static_cast<const PlanHeader *>(plan_host);
+    if (hdr->magic != kPlanMagic || hdr->version != MNB_ABI_VERSION || hdr->n_launch < 1 ||
+        hdr->n_launch > kMaxPlanLaunches)
+        return -1;
+    return hdr->n_launch;
+}
+
 int mnb_gemm_grouped(const void *plan_host, const void *plan_device, void *stream) {
     if (!plan_host || !plan_device) return MNB_ERR_NULL;
     if (!aligned16(plan_device)) return MNB_ERR_ALIGN;

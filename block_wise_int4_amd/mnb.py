@@ -55,6 +55,7 @@ _SIGNATURES = {
     "mnb_gemm": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp]),
     "mnb_plan_bytes": (_sz, [_int]),
     "mnb_plan_grouped": (_int, [ctypes.POINTER(mnb_problem), _int, _int, _int, _int, _vp, _sz]),
+    "mnb_plan_launches": (_int, [_vp]),
     "mnb_gemm_grouped": (_int, [_vp, _vp, _vp]),
 }
 
@@ -251,6 +252,11 @@ def mnb_plan_grouped(problems, block_size, dtype, device=None, bits=4):
                                                       ctypes.c_void_p(host.data_ptr()), nbytes))
     dev = host.to(device or problems[0][0].device)
     return Plan(host, dev, outs, keep)
+
+
+def mnb_plan_launches(plan):
+    """Kernel launches one mnb_gemm_grouped(plan) call issues."""
+    return lib().mnb_plan_launches(ctypes.c_void_p(plan.host.data_ptr()))
 
 
 def mnb_gemm_grouped(plan):

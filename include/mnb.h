@@ -173,6 +173,10 @@ size_t mnb_plan_bytes(int count);
 int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block_size, int dtype,
                      void *plan, size_t plan_bytes);
 
+/* Kernel launches mnb_gemm_grouped issues for a plan (one per kernel class
+ * and tile variant present), or -1 if `plan_host` is not a valid plan. Host only. */
+int mnb_plan_launches(const void *plan_host);
+
 /*
  * Run a plan. plan_host: the host image written by mnb_plan_grouped (read
  * for launch geometry); plan_device: a device copy of the same bytes (read

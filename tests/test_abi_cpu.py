@@ -127,6 +127,8 @@ def test_plan_groups_launches_by_kernel_class(L):
     assert hdr[0] == 0x4D4E4250 and hdr[2] == len(specs)
     n_launch = hdr[6]
     assert n_launch == 3        # gemv fp16, gemm M=410 tiles, gemm M=1500 tiles
+    assert L.mnb_plan_launches(buf) == 3
+    assert L.mnb_plan_launches(ctypes.create_string_buffer(64)) == -1
 
 
 def test_plan_rejects_bad_problems(L):
