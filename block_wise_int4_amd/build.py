@@ -35,40 +35,43 @@ def hipcc():
     return path
 
 
-def build(verbose=False, jobs=None):
-    """Compile every source for gfx950 and link libmnb.so in place."""
-    objdir = os.path.join(HERE, "_build")
+def build(verbose=False, jobs=None, out=None, defines=()):
+    """Compile every source for gfx950 and link libmnb.so in place (or at
+    `out`, with extra -D `defines`, for tuning experiments)."""
+    objdir = os.path.join(HERE, "_build") if out is None else out + ".objs"
     os.makedirs(objdir, exist_ok=True)
     cc = hipcc()
     objs = []
     procs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [cc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *HIPCC_FLAGS, *[f"-D{d}" for d in defines], "-I", os.path.join(ROOT, "include"), "-c",
+               os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
         objs.append(obj)
     failed = []
     for src, cmd, pr in procs:
-        out, _ = pr.communicate()
+        text, _ = pr.communicate()
         # the host pass does not know the packed-fp32 feature and says so
-        lines = [l for l in out.splitlines() if "packed-fp32-ops" not in l]
+        lines = [l for l in text.splitlines() if "packed-fp32-ops" not in l]
         if pr.returncode != 0:
             failed.append((src, "\n".join(lines)))
         elif verbose and lines:
             print("\n".join(lines))
     if failed:
         raise RuntimeError("hipcc failed:\n" + "\n\n".join(f"[{s}]\n{o}" for s, o in failed))
-    tmp = LIB + ".tmp"
+    lib = LIB if out is None else out
+    tmp = lib + ".tmp"
     cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

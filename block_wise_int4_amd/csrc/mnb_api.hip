@@ -45,7 +45,7 @@ int prepare_product(const void *x, const void *packed, const void *y, int64_t m,
     } else {
         *kind = kKindGemv;
         *variant = gemv_variant(dtype, m);
-        if (*variant == 2 && p.kg * kTileK > gemv_max_kpad(2)) *variant = 1;
+        if (*variant == 2 && p.kg * kTileK > gemv_max_kpad(2)) *variant = 3;
         if (p.kg * kTileK > gemv_max_kpad(*variant)) return MNB_ERR_SHAPE;
     }
     *out = p;
@@ -135,7 +135,8 @@ int mnb_gemv(const void *x, const void *packed, void *y, int64_t N, int64_t K, i
 
 size_t mnb_plan_bytes(int count) {
     if (count < 1 || count > kMaxPlanProblems) return 0;
-    return sizeof(PlanHeader) + sizeof(Problem) * (size_t)count;
+    return sizeof(PlanHeader) + sizeof(Problem) * (size_t)count +
+           sizeof(GemvWg) * (size_t)kGemvMaxWgs * kGemvMaxLaunches;
 }
 
 int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block_size, int dtype, void *plan,
@@ -164,6 +165,7 @@ int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block
     if (st == MNB_OK) {
         PlanHeader *hdr = static_cast<PlanHeader *>(plan);
         Problem *entries = reinterpret_cast<Problem *>(hdr + 1);
+        GemvWg *tables = reinterpret_cast<GemvWg *>(entries + count);
         memset(hdr, 0, sizeof(PlanHeader));
         hdr->magic = kPlanMagic;
         hdr->version = MNB_ABI_VERSION;
@@ -171,8 +173,8 @@ int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block
         hdr->bits = bits;
         hdr->bs = block_size;
         hdr->dtype = dtype;
-        int out = 0;
-        // gemv variants are 0..2, gemm variants 0..6: one launch per (kind, variant)
+        int out = 0, decode_tables = 0;
+        // one launch per (kind, variant) present
         for (int kind = kKindGemv; kind <= kKindGemm && st == MNB_OK; ++kind) {
             for (int v = 0; v < 8 && st == MNB_OK; ++v) {
                 PlanLaunch L{};
@@ -186,13 +188,23 @@ int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block
                     Problem p = tmp[i];
                     p.variant = v;
                     p.wg_begin = wgs;
-                    const int64_t n_wg = kind == kKindGemm ? (int64_t)p.tiles_m * p.tiles_n : gemv_workgroups(p, v);
+                    if (kind == kKindGemm) wgs += (int64_t)p.tiles_m * p.tiles_n;
+                    else if (v >= 2) wgs += gemv_workgroups(p, v);
                     if (kind == kKindGemv && gemv_lds_bytes(p, v) > lds) lds = gemv_lds_bytes(p, v);
-                    wgs += n_wg;
                     entries[out++] = p;
                 }
                 L.count = out - L.first;
                 if (L.count == 0) continue;
+                if (kind == kKindGemv && v < 2) {
+                    if (decode_tables >= kGemvMaxLaunches) {
+                        st = MNB_ERR_PLAN;
+                        break;
+                    }
+                    GemvWg *table = tables + (size_t)decode_tables * kGemvMaxWgs;
+                    wgs = gemv_schedule(entries + L.first, L.count, table, kGemvMaxWgs);
+                    L.sched_off = reinterpret_cast<uint8_t *>(table) - reinterpret_cast<uint8_t *>(hdr);
+                    ++decode_tables;
+                }
                 if (wgs > 0x7FFFFFFFLL || hdr->n_launch >= kMaxPlanLaunches) {
                     st = MNB_ERR_PLAN;
                     break;
@@ -235,7 +247,10 @@ int mnb_gemm_grouped(const void *plan_host, const void *plan_device, void *strea
         if (L.kind == kKindGemm) {
             e = launch_gemm_grouped(dev + L.first, L.count, L.wgs, L.variant, as_stream(stream));
         } else {
-            e = launch_gemv_grouped(dev + L.first, L.count, L.wgs, L.variant, (size_t)L.lds, as_stream(stream));
+            const GemvWg *table = reinterpret_cast<const GemvWg *>(static_cast<const uint8_t *>(plan_device) +
+                                                                   L.sched_off);
+            e = launch_gemv_grouped(dev + L.first, L.count, table, L.wgs, L.variant, (size_t)L.lds,
+                                    as_stream(stream));
         }
         if (e != hipSuccess) return MNB_ERR_HIP;
     }

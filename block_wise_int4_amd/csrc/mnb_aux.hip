@@ -84,39 +84,39 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t *__restri
     for (int t = 0; t < 4; ++t) dst[t] = out[t];
 }
 
-// Scales and zero points: one thread per zero-point byte of a tile (two
-// entries e = 2i, 2i+1: block jb = e / 16 of rows r and r + 1).
+// Scales and zero points: one thread per zero-point byte, i.e. per (row
+// group g, entry e, pair of tiles): entry e = jb * 16 + r is block jb of row
+// r inside each tile; tiles past kg (up to kgp) get zeros.
 template <typename T>
 __global__ __launch_bounds__(256) void pack_meta_kernel(const T *__restrict__ scales,
                                                         const uint8_t *__restrict__ zero_points, Layout L,
                                                         uint8_t *__restrict__ packed) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int per_tile = L.nbt * kTileRows / 2;
-    const int64_t tiles = L.rg * L.kg;
-    if (idx >= tiles * per_tile) return;
-    const int64_t tile = idx / per_tile;
-    const int i = (int)(idx % per_tile);
-    const int64_t g = tile / L.kg, c = tile % L.kg;
+    const int E = L.nbt * kTileRows;
+    const int64_t pairs = L.kgp / 2;
+    if (idx >= L.rg * E * pairs) return;
+    const int64_t g = idx / (E * pairs);
+    const int e = (int)((idx / pairs) % E);
+    const int64_t cp = idx % pairs;
+    const int jb = e / kTileRows, r = e % kTileRows;
+    const int64_t n = g * kTileRows + r;
     const int64_t nb = L.k / L.bs;
     const int64_t zpb = (nb + 1) / 2;
-    T *sdst = reinterpret_cast<T *>(packed + L.scales_off) + tile * L.nbt * kTileRows;
-    uint8_t *zdst = packed + L.zp_off + tile * per_tile;
+    T *sdst = reinterpret_cast<T *>(packed + L.scales_off);
     uint32_t zbyte = 0;
     for (int h = 0; h < 2; ++h) {
-        const int e = 2 * i + h;
-        const int jb = e / kTileRows, r = e % kTileRows;
-        const int64_t n = g * kTileRows + r;
+        const int64_t c = 2 * cp + h;
         const int64_t b = c * L.nbt + jb;
         T s = (T)0.0f;
         uint32_t z = 0;
-        if (n < L.n && b < nb) {
+        if (n < L.n && c < L.kg && b < nb) {
             s = scales[n * nb + b];
             z = (zero_points[n * zpb + b / 2] >> (4 * (b & 1))) & 15u;
         }
-        sdst[e] = s;
+        sdst[meta_index(g, L.nbt, L.kgp, e, c)] = s;
         zbyte |= z << (4 * h);
     }
-    zdst[i] = (uint8_t)zbyte;
+    packed[L.zp_off + meta_index(g, L.nbt, L.kgp, e, 2 * cp) / 2] = (uint8_t)zbyte;
 }
 
 // ---------------------------------------------------------------------------
@@ -142,8 +142,8 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t *__restrict__
     const int chunks_per_block = L.bs / kChunk;
     if (j % chunks_per_block == 0) {
         const int e = (j / chunks_per_block) * kTileRows + r;
-        const uint8_t *tz = packed + L.zp_off + tile * (L.nbt * kTileRows / 2);
-        zp[n * (L.k / L.bs) + k0 / L.bs] = (uint8_t)zp_nibble(tz, e);
+        const int64_t mi = meta_index(g, L.nbt, L.kgp, e, c);
+        zp[n * (L.k / L.bs) + k0 / L.bs] = (uint8_t)((packed[L.zp_off + (mi >> 1)] >> (4 * (mi & 1))) & 15u);
     }
 }
 
@@ -163,8 +163,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
     const uint4 v = *reinterpret_cast<const uint4 *>(packed + tile * kTileCodeBytes + l * 16);
     const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
     const int e = (j / (L.bs / kChunk)) * kTileRows + r;
-    const T s = reinterpret_cast<const T *>(packed + L.scales_off)[tile * L.nbt * kTileRows + e];
-    const uint32_t z = zp_nibble(packed + L.zp_off + tile * (L.nbt * kTileRows / 2), e);
+    const int64_t mi = meta_index(g, L.nbt, L.kgp, e, c);
+    const T s = reinterpret_cast<const T *>(packed + L.scales_off)[mi];
+    const uint32_t z = (packed[L.zp_off + (mi >> 1)] >> (4 * (mi & 1))) & 15u;
     T *dst = w + n * L.k + k0;
     if constexpr (sizeof(T) == 2) {
         const h2 zm = zp_magic(z);
@@ -204,7 +205,7 @@ hipError_t launch_pack(const uint8_t *qweight, const void *scales, const uint8_t
     pack_codes_kernel<<<grid_for(tiles * 64), 256, 0, st>>>(qweight, L, packed);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t meta = tiles * (L.nbt * kTileRows / 2);
+    const int64_t meta = L.rg * (L.nbt * kTileRows) * (L.kgp / 2);
     if (dtype == kF16)
         pack_meta_kernel<_Float16><<<grid_for(meta), 256, 0, st>>>((const _Float16 *)scales, zps, L, packed);
     else

@@ -89,8 +89,9 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, _Fl
             if (g < p.rg) {
                 const int64_t tile = g * p.kg + c;
                 braw[b] = *(reinterpret_cast<const uint4 *>(p.packed + tile * kTileCodeBytes) + lane);
-                sraw[b] = reinterpret_cast<const _Float16 *>(p.packed + p.scales_off)[tile * p.nbt * kTileRows + e];
-                zraw[b] = p.packed[p.zp_off + tile * (p.nbt * kTileRows / 2) + (e >> 1)];
+                const int64_t mi = meta_index(g, p.nbt, p.kgp, e, c);
+                sraw[b] = reinterpret_cast<const _Float16 *>(p.packed + p.scales_off)[mi];
+                zraw[b] = (p.packed[p.zp_off + (mi >> 1)] >> (4 * (mi & 1))) & 15u;
             } else {
                 braw[b] = {0u, 0u, 0u, 0u};
                 sraw[b] = (_Float16)0.0f;
@@ -102,7 +103,7 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, _Fl
     auto dequant_b = [&]() {
 #pragma unroll
         for (int b = 0; b < NF; ++b) {
-            const h2 zm = zp_magic((zraw[b] >> (4 * (e & 1))) & 15u);
+            const h2 zm = zp_magic(zraw[b]);
             const h2 s2 = {sraw[b], sraw[b]};
             const uint32_t w[4] = {braw[b].x, braw[b].y, braw[b].z, braw[b].w};
 #pragma unroll

@@ -1,67 +1,247 @@
-// Decode-step kernel (M = 1) and the float32 vector kernel (M >= 2).
+// Decode kernel (M = 1) and the float32 multi-row vector kernel (M >= 2).
 //
-// One wave owns one 16-row group of the weight and walks its 128-input
-// tiles: per tile each lane issues one fully coalesced 128-bit load (its row
-// r = lane & 15, chunk j = lane >> 4), one scale load and one zero-point
-// byte, turns the 32 codes into exact float16 (q - zp) pairs with the
-// 1024-offset trick, and folds them into a float32 dot product with the
-// activation slice it reads from LDS. The block scale multiplies the chunk's
-// partial sum once. After the last tile the four chunk lanes of each row are
-// summed with two cross-lane exchanges and lanes 0..15 store the 16 outputs.
+// Decode kernel. A workgroup of 4 waves walks a contiguous range of
+// "batches"; a batch is 4 consecutive 16-row groups of one weight, one per
+// wave, so the 4 waves always work on the same weight and share its
+// activation vector, staged once in LDS together with the sum of every
+// 32-input chunk. The ranges are balanced by bytes on the host, so a few
+// workgroups per CU stay busy until the end of the launch and every
+// workgroup pays the staging cost only when its range crosses into another
+// weight.
 //
-// The activation vector is staged in LDS once per workgroup (zero-filled past
-// K), so every wave of the workgroup reads it from there.
+// A wave streams its row group 8 tiles at a time: per tile one fully
+// coalesced 128-bit load per lane (row r = lane & 15, chunk j = lane >> 4),
+// and per 8 tiles one 16-byte scale load and one 4-byte zero-point load.
+// The next 8 tiles are in flight while the current ones are computed.
+//
+// Arithmetic per 32-input chunk: (w >> 4h) & 0x000F000F places two 4-bit
+// codes in the low bits of two float16 halves with a zero exponent, i.e. the
+// exact subnormals q * 2^-24; v_dot2_f32_f16 multiplies them by the
+// activation pair exactly and accumulates in float32. The zero point never
+// touches the codes: sum_k (q_k - zp) x_k = 2^24 * sum_k (q_k 2^-24) x_k
+// - zp * sum_k x_k, with the chunk sum of x read from LDS, and the block
+// scale multiplies the chunk result once. The four chunk lanes of each row
+// are summed with two cross-lane exchanges at the end of the row group.
 #include "mnb_internal.h"
 
 namespace mnb {
 
 constexpr int kGemvWaves = 4;
 constexpr int kGemvThreads = 64 * kGemvWaves;
-constexpr int kGemvUnroll = 4;  // tiles whose loads are issued together
+constexpr int kTG = kMetaGroup;  // tiles per load group (8)
 
-struct GemvTileData {
-    u32x4 codes;
-    uint32_t zb;   // zero-point byte
-    float s;
+template <typename T> struct ScaleVec;
+template <> struct ScaleVec<_Float16> {
+    u32x4 v;
+    __device__ float get(int u) const {
+        const uint32_t w = v[u >> 1];
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> (16 * (u & 1))));
+    }
+};
+template <> struct ScaleVec<float> {
+    u32x4 v[2];
+    __device__ float get(int u) const {
+        // select the vector first, then the lane: the two-subscript form
+        // v[u >> 2][u & 3] was compiled to the wrong element by this hipcc
+        const u32x4 a = v[u >> 2];
+        const uint32_t e = a[u & 3];
+        return __builtin_bit_cast(float, e);
+    }
 };
 
 template <typename T>
-__device__ __forceinline__ void gemv_load_tile(const Problem &p, int64_t g, int64_t c, int lane, int e,
-                                               GemvTileData &d) {
-    const int64_t tile = g * p.kg + c;
-    d.codes = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4 *>(p.packed + tile * kTileCodeBytes) + lane);
-    const T *sc = reinterpret_cast<const T *>(p.packed + p.scales_off) + tile * p.nbt * kTileRows + e;
-    d.s = (float)*sc;
-    d.zb = p.packed[p.zp_off + tile * (p.nbt * kTileRows / 2) + (e >> 1)];
+struct Group {
+    u32x4 codes[kTG];
+    ScaleVec<T> s;
+    uint32_t z;
+};
+
+// Loads tiles [c0, c0 + 8) of row group g (tiles past kg are not read).
+template <typename T>
+__device__ __forceinline__ void load_group(const Problem &p, int64_t g, int64_t c0, int lane, int e, Group<T> &G) {
+    const uint8_t *base = p.packed + (g * p.kg + c0) * kTileCodeBytes + lane * 16;
+    const int64_t nt = p.kg - c0;
+#pragma unroll
+    for (int u = 0; u < kTG; ++u) {
+        if (u < nt) G.codes[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + u * kTileCodeBytes));
+        else G.codes[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+    const int64_t mi = meta_index(g, p.nbt, p.kgp, e, c0);
+    G.s = *reinterpret_cast<const ScaleVec<T> *>(p.packed + p.scales_off + mi * (int64_t)sizeof(T));
+    G.z = *reinterpret_cast<const uint32_t *>(p.packed + p.zp_off + (mi >> 1));
 }
 
-template <typename T, int MR>
-__device__ __forceinline__ void gemv_tile_math(const GemvTileData &d, int e, const T *xs, int64_t kp, int64_t c,
-                                               int j, float (&acc)[MR]) {
-    const uint32_t z = (d.zb >> (4 * (e & 1))) & 15u;
-    const uint32_t w[4] = {d.codes.x, d.codes.y, d.codes.z, d.codes.w};
-    if constexpr (sizeof(T) == 2) {
-        const h2 zm = zp_magic(z);
-        h2 cp[16];
+// Contribution of tiles [c0, c0 + 8) to the lane's partial dot product.
+template <typename T>
+__device__ __forceinline__ float group_math(const Group<T> &G, int64_t nt, const T *xs, const float *xsum, int64_t c0,
+                                            int j) {
+    float acc = 0.0f;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int h = 0; h < 4; ++h) cp[4 * t + h] = centered_pair(w[t], h, zm);
-#pragma unroll
-        for (int row = 0; row < MR; ++row) {
-            const uint4 *xv = reinterpret_cast<const uint4 *>(xs + row * kp + c * kTileK + j * kChunk);
-            float part = 0.0f;
+    for (int u = 0; u < kTG; ++u) {
+        if (u >= nt) break;
+        const int64_t c = c0 + u;
+        const float s = G.s.get(u);
+        const float zs = (float)((G.z >> (4 * u)) & 15u) * xsum[c * 4 + j];
+        const u32x4 w = G.codes[u];
+        float part = 0.0f;
+        if constexpr (sizeof(T) == 2) {
+            const u32x4 *xv = reinterpret_cast<const u32x4 *>(xs + c * kTileK + j * kChunk);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const uint4 xx = xv[t];
-                const uint32_t xw[4] = {xx.x, xx.y, xx.z, xx.w};
+                const u32x4 xx = xv[t];
 #pragma unroll
-                for (int h = 0; h < 4; ++h) part = __builtin_amdgcn_fdot2(cp[4 * t + h], as_h2(xw[h]), part, false);
+                for (int h = 0; h < 4; ++h)
+                    part = __builtin_amdgcn_fdot2(as_h2((w[t] >> (4 * h)) & 0x000F000Fu), as_h2(xx[h]), part, false);
             }
-            acc[row] = __builtin_fmaf(d.s, part, acc[row]);
+            part = __builtin_fmaf(part, 16777216.0f, -zs);  // 2^24 undoes the subnormal scaling exactly
+        } else {
+            const float4 *xv = reinterpret_cast<const float4 *>(xs + c * kTileK + j * kChunk);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float4 xa = xv[2 * t], xb = xv[2 * t + 1];
+                const float xf[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+                for (int u2 = 0; u2 < 8; ++u2) part = __builtin_fmaf((float)code_at(w[t], u2), xf[u2], part);
+            }
+            part -= zs;
         }
-    } else {
+        acc = __builtin_fmaf(s, part, acc);
+    }
+    return acc;
+}
+
+// Stage x[0 .. K) (zero-filled to K_pad) and its 32-input chunk sums in LDS.
+template <typename T>
+__device__ __forceinline__ void stage_x(const Problem &p, T *xs, float *xsum) {
+    __syncthreads();  // every wave is done with the previous vector
+    const int64_t kp = p.kg * kTileK;
+    const T *x = static_cast<const T *>(p.x);
+    constexpr int kPer = 16 / sizeof(T);
+    for (int64_t i = threadIdx.x; i < kp / kPer; i += kGemvThreads) {
+        const int64_t k = i * kPer;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (k < p.k) v = *reinterpret_cast<const u32x4 *>(x + k);
+        *reinterpret_cast<u32x4 *>(xs + k) = v;
+    }
+    __syncthreads();
+    for (int64_t ch = threadIdx.x; ch < kp / kChunk; ch += kGemvThreads) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) sum += (float)xs[ch * kChunk + i];
+        xsum[ch] = sum;
+    }
+    __syncthreads();
+}
+
+// Runs batches [b0, b1) starting in problem `pi`.
+template <typename T, bool kGrouped>
+__device__ __forceinline__ void decode_range(const Problem *entries, Problem p, int pi, int64_t b0, int64_t b1,
+                                             uint8_t *smem) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, j = lane >> 4;
+    int64_t b = b0;
+    while (b < b1) {
+        if constexpr (kGrouped) {
+            while (b >= p.batch_end) p = entries[++pi];
+        }
+        const int64_t bend = b1 < p.batch_end ? b1 : p.batch_end;
+        const int64_t kp = p.kg * kTileK;
+        T *xs = reinterpret_cast<T *>(smem);
+        float *xsum = reinterpret_cast<float *>(smem + kp * sizeof(T));
+        const int e = (j / (p.bs / kChunk)) * kTileRows + r;
+        const int64_t ngroups = (p.kg + kTG - 1) / kTG;
+
+        int64_t sb = b, g = (b - p.batch_begin) * kGemvWaves + wave;
+        int64_t c0 = 0;
+        bool have = g < p.rg;
+        Group<T> cur, nxt;
+        if (have) load_group<T>(p, g, 0, lane, e, cur);
+        stage_x<T>(p, xs, xsum);
+
+        float acc = 0.0f;
+        while (have) {
+            // the step after this one: next 8 tiles, or the next batch's row group
+            int64_t nb = sb, nc0 = c0 + kTG;
+            if (nc0 >= ngroups * kTG) {
+                nc0 = 0;
+                nb = sb + 1;
+            }
+            const int64_t ng = (nb - p.batch_begin) * kGemvWaves + wave;
+            const bool nvalid = nb < bend && ng < p.rg;
+            if (nvalid) load_group<T>(p, ng, nc0, lane, e, nxt);
+            acc += group_math<T>(cur, p.kg - c0, xs, xsum, c0, j);
+            if (nc0 == 0) {  // row group finished
+                float v = acc;
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+                const int64_t n = g * kTileRows + r;
+                if (j == 0 && n < p.n) static_cast<T *>(p.y)[n] = (T)v;
+                acc = 0.0f;
+            }
+            if (!nvalid) break;
+            cur = nxt;
+            sb = nb;
+            c0 = nc0;
+            g = ng;
+        }
+        b = bend;
+    }
+}
+
+#ifndef MNB_DECODE_OCC
+#define MNB_DECODE_OCC 2
+#endif
+
+template <typename T>
+__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(MNB_DECODE_OCC)))
+void decode_kernel(Problem p, int64_t wgs) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int64_t nbat = p.batch_end;  // batch_begin = 0 for a single problem
+    const int64_t b0 = nbat * blockIdx.x / wgs, b1 = nbat * (blockIdx.x + 1) / wgs;
+    decode_range<T, false>(nullptr, p, 0, b0, b1, smem);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(MNB_DECODE_OCC)))
+void decode_grouped_kernel(const Problem *entries, const GemvWg *table) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    const GemvWg w = table[blockIdx.x];
+    if (w.b0 >= w.b1) return;
+    decode_range<T, true>(entries, entries[w.p], w.p, w.b0, w.b1, smem);
+}
+
+// ---------------------------------------------------------------------------
+// float32 multi-row kernel (M >= 2): one wave per row group, 4 activation
+// rows per pass, activations staged in LDS.
+// ---------------------------------------------------------------------------
+template <int MR>
+__device__ __forceinline__ void rows_workgroup(const Problem &p, int64_t wg, float *xs) {
+    const int64_t mchunks = (p.m + MR - 1) / MR;
+    const int64_t wq = wg / mchunks;
+    const int64_t m0 = (wg % mchunks) * MR;
+    const int64_t kp = p.kg * kTileK;
+    const float *x = static_cast<const float *>(p.x);
+    for (int64_t i = threadIdx.x; i < MR * kp / 4; i += kGemvThreads) {
+        const int64_t row = i / (kp / 4);
+        const int64_t k = (i % (kp / 4)) * 4;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (m0 + row < p.m && k < p.k) v = *reinterpret_cast<const u32x4 *>(x + (m0 + row) * p.k + k);
+        *reinterpret_cast<u32x4 *>(xs + row * kp + k) = v;
+    }
+    __syncthreads();
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, j = lane >> 4;
+    const int64_t g = wq * kGemvWaves + wave;
+    if (g >= p.rg) return;
+    const int e = (j / (p.bs / kChunk)) * kTileRows + r;
+    float acc[MR];
+#pragma unroll
+    for (int row = 0; row < MR; ++row) acc[row] = 0.0f;
+    for (int64_t c = 0; c < p.kg; ++c) {
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(p.packed + (g * p.kg + c) * kTileCodeBytes + lane * 16);
+        const int64_t mi = meta_index(g, p.nbt, p.kgp, e, c);
+        const float s = reinterpret_cast<const float *>(p.packed + p.scales_off)[mi];
+        const uint32_t z = (p.packed[p.zp_off + (mi >> 1)] >> (4 * (mi & 1))) & 15u;
         float dv[32];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -69,68 +249,13 @@ __device__ __forceinline__ void gemv_tile_math(const GemvTileData &d, int e, con
             for (int u = 0; u < 8; ++u) dv[8 * t + u] = (float)((int)code_at(w[t], u) - (int)z);
 #pragma unroll
         for (int row = 0; row < MR; ++row) {
-            const float4 *xv = reinterpret_cast<const float4 *>(xs + row * kp + c * kTileK + j * kChunk);
+            const float *xr = xs + row * kp + c * kTileK + j * kChunk;
             float part = 0.0f;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const float4 xx = xv[q];
-                part = __builtin_fmaf(dv[4 * q + 0], xx.x, part);
-                part = __builtin_fmaf(dv[4 * q + 1], xx.y, part);
-                part = __builtin_fmaf(dv[4 * q + 2], xx.z, part);
-                part = __builtin_fmaf(dv[4 * q + 3], xx.w, part);
-            }
-            acc[row] = __builtin_fmaf(d.s, part, acc[row]);
+            for (int i = 0; i < 32; ++i) part = __builtin_fmaf(dv[i], xr[i], part);
+            acc[row] = __builtin_fmaf(s, part, acc[row]);
         }
     }
-}
-
-// One workgroup: row groups [4 * wq, 4 * wq + 4) of the weight, activation
-// rows [m0, m0 + MR).
-template <typename T, int MR>
-__device__ __forceinline__ void gemv_workgroup(const Problem &p, int64_t wg, T *xs) {
-    const int64_t mchunks = (p.m + MR - 1) / MR;
-    const int64_t wq = wg / mchunks;
-    const int64_t m0 = (wg % mchunks) * MR;
-    const int64_t kp = p.kg * kTileK;
-    const T *x = static_cast<const T *>(p.x);
-
-    // Stage X[m0 .. m0 + MR) into LDS in 16-byte pieces, zero past K and M.
-    constexpr int kPer = 16 / sizeof(T);
-    const int64_t pieces = MR * kp / kPer;
-    for (int64_t i = threadIdx.x; i < pieces; i += kGemvThreads) {
-        const int64_t row = i / (kp / kPer);
-        const int64_t k = (i % (kp / kPer)) * kPer;
-        uint4 v = {0u, 0u, 0u, 0u};
-        if (m0 + row < p.m && k < p.k) v = *reinterpret_cast<const uint4 *>(x + (m0 + row) * p.k + k);
-        *reinterpret_cast<uint4 *>(xs + row * kp + k) = v;
-    }
-    __syncthreads();
-
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int r = lane & 15, j = lane >> 4;
-    const int64_t g = wq * kGemvWaves + wave;
-    if (g >= p.rg) return;
-    const int e = (j / (p.bs / kChunk)) * kTileRows + r;
-
-    float acc[MR];
-#pragma unroll
-    for (int row = 0; row < MR; ++row) acc[row] = 0.0f;
-
-    int64_t c = 0;
-    for (; c + kGemvUnroll <= p.kg; c += kGemvUnroll) {
-        GemvTileData d[kGemvUnroll];
-#pragma unroll
-        for (int u = 0; u < kGemvUnroll; ++u) gemv_load_tile<T>(p, g, c + u, lane, e, d[u]);
-#pragma unroll
-        for (int u = 0; u < kGemvUnroll; ++u) gemv_tile_math<T, MR>(d[u], e, xs, kp, c + u, j, acc);
-    }
-    for (; c < p.kg; ++c) {
-        GemvTileData d;
-        gemv_load_tile<T>(p, g, c, lane, e, d);
-        gemv_tile_math<T, MR>(d, e, xs, kp, c, j, acc);
-    }
-
 #pragma unroll
     for (int row = 0; row < MR; ++row) {
         float v = acc[row];
@@ -140,21 +265,19 @@ __device__ __forceinline__ void gemv_workgroup(const Problem &p, int64_t wg, T *
     }
     const int64_t n = g * kTileRows + r;
     if (j == 0 && n < p.n) {
-        T *y = static_cast<T *>(p.y);
+        float *y = static_cast<float *>(p.y);
 #pragma unroll
         for (int row = 0; row < MR; ++row)
-            if (m0 + row < p.m) y[(m0 + row) * p.n + n] = (T)acc[row];
+            if (m0 + row < p.m) y[(m0 + row) * p.n + n] = acc[row];
     }
 }
 
-template <typename T, int MR>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(Problem p) {
+template <int MR>
+__global__ __launch_bounds__(kGemvThreads) void rows_kernel(Problem p) {
     extern __shared__ __align__(16) uint8_t smem[];
-    gemv_workgroup<T, MR>(p, blockIdx.x, reinterpret_cast<T *>(smem));
+    rows_workgroup<MR>(p, blockIdx.x, reinterpret_cast<float *>(smem));
 }
 
-// Index of the problem owning workgroup `wg`: the last entry whose wg_begin
-// is <= wg (entries are sorted by wg_begin).
 __device__ __forceinline__ int find_problem(const Problem *entries, int count, int64_t wg) {
     int lo = 0, hi = count - 1;
     while (lo < hi) {
@@ -165,57 +288,137 @@ __device__ __forceinline__ int find_problem(const Problem *entries, int count, i
     return lo;
 }
 
-template <typename T, int MR>
-__global__ __launch_bounds__(kGemvThreads) void gemv_grouped_kernel(const Problem *entries, int count) {
+template <int MR>
+__global__ __launch_bounds__(kGemvThreads) void rows_grouped_kernel(const Problem *entries, int count) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int i = find_problem(entries, count, blockIdx.x);
     const Problem p = entries[i];
-    gemv_workgroup<T, MR>(p, (int64_t)blockIdx.x - p.wg_begin, reinterpret_cast<T *>(smem));
+    rows_workgroup<MR>(p, (int64_t)blockIdx.x - p.wg_begin, reinterpret_cast<float *>(smem));
 }
 
-// Variants: 0 = fp16 x1, 1 = fp32 x1, 2 = fp32 x4 activation rows per pass.
-constexpr int kGemvMaxLds = 65536;
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+constexpr int kRowsMR = 4;
+constexpr int kGemvMaxLds = 160 * 1024;     // LDS of one CU
+constexpr int kDefaultLds = 64 * 1024;      // above this a launch must opt in
 
+// Variants: 0 = fp16 decode, 1 = fp32 decode, 2 = fp32 4 rows per pass,
+// 3 = fp32 1 row per pass (K too long to stage 4 rows).
 int gemv_variant(int dtype, int64_t m) {
-    if (dtype == kF16) return 0;
-    return m >= 2 ? 2 : 1;
+    if (m >= 2) return 2;
+    return dtype == kF16 ? 0 : 1;
 }
 
-static int gemv_rows(int variant) { return variant == 2 ? 4 : 1; }
-static int gemv_elem(int variant) { return variant == 0 ? 2 : 4; }
+static int elem_bytes(int variant) { return variant == 0 ? 2 : 4; }
+static int rows_per_pass(int variant) { return variant == 2 ? kRowsMR : 1; }
 
-static size_t gemv_lds(const Problem &p, int variant) {
-    return (size_t)gemv_rows(variant) * (size_t)(p.kg * kTileK) * gemv_elem(variant);
+size_t gemv_lds_bytes(const Problem &p, int variant) {
+    const int64_t kp = p.kg * kTileK;
+    if (variant >= 2) return (size_t)(rows_per_pass(variant) * kp * 4);
+    return (size_t)(kp * elem_bytes(variant) + kp / kChunk * 4);
+}
+
+int64_t gemv_max_kpad(int variant) {
+    if (variant >= 2) return kGemvMaxLds / (rows_per_pass(variant) * 4);
+    return (int64_t)(kGemvMaxLds / (elem_bytes(variant) + 4.0 / kChunk));
 }
 
 int64_t gemv_workgroups(const Problem &p, int variant) {
-    const int mr = gemv_rows(variant);
+    const int mr = rows_per_pass(variant);
     return ((p.rg + kGemvWaves - 1) / kGemvWaves) * ((p.m + mr - 1) / mr);
 }
 
-// Largest K (padded) the LDS staging allows for a variant.
-int64_t gemv_max_kpad(int variant) { return kGemvMaxLds / (gemv_rows(variant) * gemv_elem(variant)); }
+// Kernels whose dynamic LDS exceeds the default must say so once per size.
+template <typename K>
+static hipError_t allow_lds(K kernel, size_t lds) {
+    if (lds <= (size_t)kDefaultLds) return hipSuccess;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)lds);
+}
 
-hipError_t launch_gemv(const Problem &p, int dtype, int variant, hipStream_t st) {
+int64_t gemv_schedule(Problem *entries, int count, GemvWg *table, int max_wgs) {
+    // batches and their cost (tiles per row group, plus one for the row end)
+    int64_t nbat = 0, cost = 0;
+    for (int i = 0; i < count; ++i) {
+        Problem &p = entries[i];
+        p.batch_begin = nbat;
+        nbat += (p.rg + kGemvWaves - 1) / kGemvWaves;
+        p.batch_end = nbat;
+        cost += (p.batch_end - p.batch_begin) * (p.kg + 1);
+    }
+    const int64_t wgs = nbat < max_wgs ? nbat : max_wgs;
+    // workgroup w starts at the first batch whose cost prefix reaches w * cost / wgs
+    int pi = 0;
+    int64_t b = 0, prefix = 0;
+    for (int64_t w = 0; w <= wgs; ++w) {
+        const int64_t target = cost * w / wgs;
+        while (b < nbat && prefix < target) {
+            while (b >= entries[pi].batch_end) ++pi;
+            prefix += entries[pi].kg + 1;
+            ++b;
+        }
+        if (w < wgs) {
+            int q = pi;
+            while (q < count - 1 && b >= entries[q].batch_end) ++q;
+            table[w].b0 = (int32_t)b;
+            table[w].p = q;
+            table[w].pad_ = 0;
+        }
+        if (w > 0) table[w - 1].b1 = (int32_t)b;
+    }
+    return wgs;
+}
+
+hipError_t launch_gemv(const Problem &p0, int dtype, int variant, hipStream_t st) {
     (void)dtype;
-    const unsigned grid = (unsigned)gemv_workgroups(p, variant);
-    const size_t lds = gemv_lds(p, variant);
-    switch (variant) {
-    case 0: gemv_kernel<_Float16, 1><<<grid, kGemvThreads, lds, st>>>(p); break;
-    case 1: gemv_kernel<float, 1><<<grid, kGemvThreads, lds, st>>>(p); break;
-    default: gemv_kernel<float, 4><<<grid, kGemvThreads, lds, st>>>(p); break;
+    const size_t lds = gemv_lds_bytes(p0, variant);
+    hipError_t e = hipSuccess;
+    if (variant >= 2) {
+        const unsigned grid = (unsigned)gemv_workgroups(p0, variant);
+        if (variant == 2) {
+            if ((e = allow_lds(rows_kernel<kRowsMR>, lds)) != hipSuccess) return e;
+            rows_kernel<kRowsMR><<<grid, kGemvThreads, lds, st>>>(p0);
+        } else {
+            if ((e = allow_lds(rows_kernel<1>, lds)) != hipSuccess) return e;
+            rows_kernel<1><<<grid, kGemvThreads, lds, st>>>(p0);
+        }
+        return hipGetLastError();
+    }
+    Problem p = p0;
+    p.batch_begin = 0;
+    p.batch_end = (p.rg + kGemvWaves - 1) / kGemvWaves;
+    const int64_t wgs = p.batch_end < kGemvMaxWgs ? p.batch_end : kGemvMaxWgs;
+    if (variant == 0) {
+        if ((e = allow_lds(decode_kernel<_Float16>, lds)) != hipSuccess) return e;
+        decode_kernel<_Float16><<<(unsigned)wgs, kGemvThreads, lds, st>>>(p, wgs);
+    } else {
+        if ((e = allow_lds(decode_kernel<float>, lds)) != hipSuccess) return e;
+        decode_kernel<float><<<(unsigned)wgs, kGemvThreads, lds, st>>>(p, wgs);
     }
     return hipGetLastError();
 }
 
-size_t gemv_lds_bytes(const Problem &p, int variant) { return gemv_lds(p, variant); }
-
-hipError_t launch_gemv_grouped(const Problem *dev_entries, int count, int64_t wgs, int variant, size_t lds,
-                               hipStream_t st) {
+hipError_t launch_gemv_grouped(const Problem *dev_entries, int count, const GemvWg *dev_table, int64_t wgs,
+                               int variant, size_t lds, hipStream_t st) {
+    hipError_t e = hipSuccess;
     switch (variant) {
-    case 0: gemv_grouped_kernel<_Float16, 1><<<(unsigned)wgs, kGemvThreads, lds, st>>>(dev_entries, count); break;
-    case 1: gemv_grouped_kernel<float, 1><<<(unsigned)wgs, kGemvThreads, lds, st>>>(dev_entries, count); break;
-    default: gemv_grouped_kernel<float, 4><<<(unsigned)wgs, kGemvThreads, lds, st>>>(dev_entries, count); break;
+    case 0:
+        if ((e = allow_lds(decode_grouped_kernel<_Float16>, lds)) != hipSuccess) return e;
+        decode_grouped_kernel<_Float16><<<(unsigned)wgs, kGemvThreads, lds, st>>>(dev_entries, dev_table);
+        break;
+    case 1:
+        if ((e = allow_lds(decode_grouped_kernel<float>, lds)) != hipSuccess) return e;
+        decode_grouped_kernel<float><<<(unsigned)wgs, kGemvThreads, lds, st>>>(dev_entries, dev_table);
+        break;
+    case 2:
+        if ((e = allow_lds(rows_grouped_kernel<kRowsMR>, lds)) != hipSuccess) return e;
+        rows_grouped_kernel<kRowsMR><<<(unsigned)wgs, kGemvThreads, lds, st>>>(dev_entries, count);
+        break;
+    default:
+        if ((e = allow_lds(rows_grouped_kernel<1>, lds)) != hipSuccess) return e;
+        rows_grouped_kernel<1><<<(unsigned)wgs, kGemvThreads, lds, st>>>(dev_entries, count);
+        break;
     }
     return hipGetLastError();
 }

@@ -19,9 +19,11 @@ struct Problem {
     const uint8_t *packed;
     void *y;
     int64_t m, n, k;
-    int64_t rg, kg;          // tile grid of the packed weight
+    int64_t rg, kg, kgp;     // tile grid of the packed weight, metadata stride
     int64_t scales_off, zp_off;
     int64_t wg_begin;        // first workgroup of this problem inside its launch
+    int64_t batch_begin;     // decode kernel: first 4-row-group batch in its launch
+    int64_t batch_end;
     int32_t bs, nbt;
     int32_t variant;         // kernel variant index (see mnb_gemm.hip / mnb_gemv.hip)
     int32_t tiles_m, tiles_n;
@@ -38,7 +40,19 @@ struct PlanLaunch {
     int32_t count;
     int64_t wgs;             // workgroups of this launch
     int64_t lds;             // dynamic LDS bytes (gemv launches)
+    int64_t sched_off;       // decode launches: byte offset of the workgroup table
 };
+
+// Decode kernel schedule: workgroup w runs batches [b0, b1) (a batch is 4
+// row groups of one problem, one per wave), starting in problem p.
+struct GemvWg {
+    int32_t b0, b1, p, pad_;
+};
+#ifndef MNB_DECODE_WGS
+#define MNB_DECODE_WGS 512
+#endif
+constexpr int kGemvMaxWgs = MNB_DECODE_WGS;  // resident workgroups (2 per CU on 256 CUs)
+constexpr int kGemvMaxLaunches = 3;
 
 constexpr uint32_t kPlanMagic = 0x4D4E4250u;  // "PBNM"
 constexpr int kMaxPlanLaunches = 16;
@@ -67,6 +81,7 @@ inline Problem make_problem(const void *x, const void *packed, void *y, int64_t 
     p.k = k;
     p.rg = L.rg;
     p.kg = L.kg;
+    p.kgp = L.kgp;
     p.scales_off = L.scales_off;
     p.zp_off = L.zp_off;
     p.bs = bs;
@@ -82,14 +97,18 @@ hipError_t launch_pack(const uint8_t *qweight, const void *scales, const uint8_t
 hipError_t launch_unpack(const uint8_t *packed, const Layout &L, uint8_t *q, uint8_t *zp, hipStream_t st);
 hipError_t launch_dequant(const uint8_t *packed, const Layout &L, int dtype, void *w, hipStream_t st);
 
-// GEMV / vector kernel: M = 1 (fp16, fp32) and fp32 with M >= 2.
+// Decode kernel (M = 1, fp16 and fp32) and the fp32 multi-row vector kernel
+// (fp32, M >= 2). Variants: 0 = fp16 decode, 1 = fp32 decode, 2 = fp32 rows.
 int gemv_variant(int dtype, int64_t m);
-int64_t gemv_workgroups(const Problem &p, int variant);
+int64_t gemv_workgroups(const Problem &p, int variant);   // variant 2 only
 int64_t gemv_max_kpad(int variant);
 size_t gemv_lds_bytes(const Problem &p, int variant);
+// Decode schedule for a list of problems (host): fills batch_begin/end of
+// each problem and the workgroup table; returns the workgroup count.
+int64_t gemv_schedule(Problem *entries, int count, GemvWg *table, int max_wgs);
 hipError_t launch_gemv(const Problem &p, int dtype, int variant, hipStream_t st);
-hipError_t launch_gemv_grouped(const Problem *dev_entries, int count, int64_t wgs, int variant, size_t lds,
-                               hipStream_t st);
+hipError_t launch_gemv_grouped(const Problem *dev_entries, int count, const GemvWg *dev_table, int64_t wgs,
+                               int variant, size_t lds, hipStream_t st);
 
 // MFMA kernel: fp16 with M >= 2.
 int gemm_variant(int64_t m);

@@ -19,8 +19,9 @@
  * ---------------------------------------
  *  - Pointers named x, y, w, qweight, scales, zero_points, packed, q, zp are
  *    DEVICE pointers. The caller owns all memory; the library allocates,
- *    frees and synchronizes nothing, and keeps no mutable global state, so
- *    calls are reentrant. Calls on one stream run in order.
+ *    frees and synchronizes nothing and keeps no state between calls (beyond
+ *    raising a kernel's LDS limit the first time a long K needs it), so calls
+ *    are reentrant. Calls on one stream run in order.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call that touches device memory is asynchronous on it.
  *  - bits must be 4, block_size 32 or 64, K a positive multiple of

@@ -45,10 +45,11 @@ def _expected_bytes(n, k, bs, sb):
     def up(v, a=256):
         return (v + a - 1) // a * a
     rg, kg = math.ceil(n / 16), math.ceil(k / 128)
-    tiles = rg * kg
-    codes = up(tiles * 1024)
-    scales = up(codes + tiles * (128 // bs) * 16 * sb)
-    return up(scales + tiles * (128 // bs) * 8)
+    kgp = math.ceil(kg / 8) * 8           # per-entry metadata padded to 8 tiles
+    entries = rg * (128 // bs) * 16
+    codes = up(rg * kg * 1024)
+    scales = up(codes + entries * kgp * sb)
+    return up(scales + entries * kgp // 2)
 
 
 @pytest.mark.parametrize("n,k,bs,dt", [(3072, 1024, 32, 0), (151936, 1024, 32, 1), (768, 3072, 64, 1),
@@ -98,9 +99,10 @@ def test_invalid_arguments_are_rejected_before_launch(L, call, status):
     assert call(L) == status
 
 
-def test_fp32_k_limit(L):
-    # float32 stages K inputs in 64 KB of LDS: K up to 16384
-    assert L.mnb_gemv(FAKE, FAKE2, FAKE3, 64, 16384 + 128, 4, 32, 0, None) == SHAPE
+def test_k_limit(L):
+    # K up to MNB_MAX_K = 32768 inputs for both dtypes
+    assert L.mnb_gemv(FAKE, FAKE2, FAKE3, 64, 32768 + 32, 4, 32, 0, None) == SHAPE
+    assert L.mnb_gemm(FAKE, FAKE2, FAKE3, 4, 64, 32768 + 64, 4, 64, 1, None) == SHAPE
 
 
 def _problems(specs):

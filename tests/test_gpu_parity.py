@@ -96,7 +96,8 @@ def run_product(m, n, k, bs, dt, seed, std=0.02):
 GEMV_CASES = [(3072, 1024, 32, np.float32), (1, 32, 32, np.float16), (17, 96, 32, np.float16),
               (100, 192, 64, np.float16), (64, 2048, 32, np.float16), (300, 4160, 32, np.float16),
               (33, 8192, 32, np.float32), (2048, 1024, 32, np.float16), (5, 32768, 32, np.float16),
-              (250, 736, 32, np.float32), (96, 768, 64, np.float32)]
+              (250, 736, 32, np.float32), (96, 768, 64, np.float32), (7, 32768, 32, np.float32),
+              (3072, 1024, 32, np.float16), (1024, 6144, 64, np.float16)]
 
 
 @pytest.mark.parametrize("n,k,bs,dt", GEMV_CASES)
@@ -119,7 +120,8 @@ def test_gemm_fp16_parity(m, n, k, bs):
     assert ok, f"max err {err:.3e} vs 2e-3 * {mx:.3e}"
 
 
-@pytest.mark.parametrize("m,n,k,bs", [(2, 64, 1024, 32), (5, 100, 4096, 32), (3, 40, 8192, 64), (9, 17, 96, 32)])
+@pytest.mark.parametrize("m,n,k,bs", [(2, 64, 1024, 32), (5, 100, 4096, 32), (3, 40, 8192, 64), (9, 17, 96, 32),
+                                      (3, 40, 16384, 32), (6, 20, 32768, 64)])
 def test_gemm_fp32_parity(m, n, k, bs):
     y, ref = run_product(m, n, k, bs, np.float32, seed=m + n + k)
     ok, err, mx = oracle.within_tolerance(y, ref, TOL[np.float32])
