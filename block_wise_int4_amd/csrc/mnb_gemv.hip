@@ -28,50 +28,78 @@ namespace mnb {
 
 constexpr int kGemvWaves = 4;
 constexpr int kGemvThreads = 64 * kGemvWaves;
-constexpr int kTG = kMetaGroup;  // tiles per load group (8)
+#ifndef MNB_DECODE_TG
+#define MNB_DECODE_TG 8
+#endif
+constexpr int kTG = MNB_DECODE_TG;  // tiles per load group (4 or 8; divides the metadata group)
+static_assert(kMetaGroup % kTG == 0, "load groups must not straddle metadata groups");
 
-template <typename T> struct ScaleVec;
-template <> struct ScaleVec<_Float16> {
-    u32x4 v;
-    __device__ float get(int u) const {
-        const uint32_t w = v[u >> 1];
-        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> (16 * (u & 1))));
+#ifndef MNB_DECODE_TWO_MASK
+#define MNB_DECODE_TWO_MASK 1
+#endif
+#ifndef MNB_DECODE_NT
+#define MNB_DECODE_NT 1
+#endif
+
+// Scales of TG consecutive tiles, read with one vector load.
+template <typename T, int TG>
+struct ScaleVec {
+    static constexpr int kWords = TG * (int)sizeof(T) / 4;
+    uint32_t w[kWords];
+    __device__ void load(const uint8_t *p) {
+        if constexpr (kWords == 2) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(p);
+            w[0] = v.x;
+            w[1] = v.y;
+        } else {
+#pragma unroll
+            for (int i = 0; i < kWords / 4; ++i) {
+                const u32x4 v = reinterpret_cast<const u32x4 *>(p)[i];
+                w[4 * i + 0] = v.x;
+                w[4 * i + 1] = v.y;
+                w[4 * i + 2] = v.z;
+                w[4 * i + 3] = v.w;
+            }
+        }
     }
-};
-template <> struct ScaleVec<float> {
-    u32x4 v[2];
     __device__ float get(int u) const {
-        // select the vector first, then the lane: the two-subscript form
-        // v[u >> 2][u & 3] was compiled to the wrong element by this hipcc
-        const u32x4 a = v[u >> 2];
-        const uint32_t e = a[u & 3];
-        return __builtin_bit_cast(float, e);
+        if constexpr (sizeof(T) == 2) {
+            const uint32_t x = w[u >> 1];
+            return (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> (16 * (u & 1))));
+        } else {
+            return __builtin_bit_cast(float, w[u]);
+        }
     }
 };
 
 template <typename T>
 struct Group {
     u32x4 codes[kTG];
-    ScaleVec<T> s;
+    ScaleVec<T, kTG> s;
     uint32_t z;
 };
 
-// Loads tiles [c0, c0 + 8) of row group g (tiles past kg are not read).
+// Loads tiles [c0, c0 + kTG) of row group g (tiles past kg are not read).
 template <typename T>
 __device__ __forceinline__ void load_group(const Problem &p, int64_t g, int64_t c0, int lane, int e, Group<T> &G) {
     const uint8_t *base = p.packed + (g * p.kg + c0) * kTileCodeBytes + lane * 16;
     const int64_t nt = p.kg - c0;
 #pragma unroll
     for (int u = 0; u < kTG; ++u) {
+#if MNB_DECODE_NT
         if (u < nt) G.codes[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + u * kTileCodeBytes));
+#else
+        if (u < nt) G.codes[u] = *reinterpret_cast<const u32x4 *>(base + u * kTileCodeBytes);
+#endif
         else G.codes[u] = u32x4{0u, 0u, 0u, 0u};
     }
     const int64_t mi = meta_index(g, p.nbt, p.kgp, e, c0);
-    G.s = *reinterpret_cast<const ScaleVec<T> *>(p.packed + p.scales_off + mi * (int64_t)sizeof(T));
-    G.z = *reinterpret_cast<const uint32_t *>(p.packed + p.zp_off + (mi >> 1));
+    G.s.load(p.packed + p.scales_off + mi * (int64_t)sizeof(T));
+    if constexpr (kTG == 8) G.z = *reinterpret_cast<const uint32_t *>(p.packed + p.zp_off + (mi >> 1));
+    else G.z = *reinterpret_cast<const uint16_t *>(p.packed + p.zp_off + (mi >> 1));
 }
 
-// Contribution of tiles [c0, c0 + 8) to the lane's partial dot product.
+// Contribution of tiles [c0, c0 + kTG) to the lane's partial dot product.
 template <typename T>
 __device__ __forceinline__ float group_math(const Group<T> &G, int64_t nt, const T *xs, const float *xsum, int64_t c0,
                                             int j) {
@@ -86,6 +114,22 @@ __device__ __forceinline__ float group_math(const Group<T> &G, int64_t nt, const
         float part = 0.0f;
         if constexpr (sizeof(T) == 2) {
             const u32x4 *xv = reinterpret_cast<const u32x4 *>(xs + c * kTileK + j * kChunk);
+#if MNB_DECODE_TWO_MASK
+            // pairs 0 and 2 masked in place (q * 2^-24), pairs 1 and 3 masked
+            // one nibble higher (q * 2^-20) into a second sum scaled back by
+            // 1/16 at the end: one shift per word instead of three
+            float part_hi = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const u32x4 xx = xv[t];
+                const uint32_t w0 = w[t], w8 = w[t] >> 8;
+                part = __builtin_amdgcn_fdot2(as_h2(w0 & 0x000F000Fu), as_h2(xx[0]), part, false);
+                part_hi = __builtin_amdgcn_fdot2(as_h2(w0 & 0x00F000F0u), as_h2(xx[1]), part_hi, false);
+                part = __builtin_amdgcn_fdot2(as_h2(w8 & 0x000F000Fu), as_h2(xx[2]), part, false);
+                part_hi = __builtin_amdgcn_fdot2(as_h2(w8 & 0x00F000F0u), as_h2(xx[3]), part_hi, false);
+            }
+            part = __builtin_fmaf(part_hi, 0.0625f, part);
+#else
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const u32x4 xx = xv[t];
@@ -93,6 +137,7 @@ __device__ __forceinline__ float group_math(const Group<T> &G, int64_t nt, const
                 for (int h = 0; h < 4; ++h)
                     part = __builtin_amdgcn_fdot2(as_h2((w[t] >> (4 * h)) & 0x000F000Fu), as_h2(xx[h]), part, false);
             }
+#endif
             part = __builtin_fmaf(part, 16777216.0f, -zs);  // 2^24 undoes the subnormal scaling exactly
         } else {
             const float4 *xv = reinterpret_cast<const float4 *>(xs + c * kTileK + j * kChunk);
@@ -189,7 +234,7 @@ __device__ __forceinline__ void decode_range(const Problem *entries, Problem p, 
 }
 
 #ifndef MNB_DECODE_OCC
-#define MNB_DECODE_OCC 2
+#define MNB_DECODE_OCC 3
 #endif
 
 template <typename T>

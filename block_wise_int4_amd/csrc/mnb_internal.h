@@ -49,9 +49,9 @@ struct GemvWg {
     int32_t b0, b1, p, pad_;
 };
 #ifndef MNB_DECODE_WGS
-#define MNB_DECODE_WGS 512
+#define MNB_DECODE_WGS 768
 #endif
-constexpr int kGemvMaxWgs = MNB_DECODE_WGS;  // resident workgroups (2 per CU on 256 CUs)
+constexpr int kGemvMaxWgs = MNB_DECODE_WGS;  // resident workgroups (3 per CU on 256 CUs)
 constexpr int kGemvMaxLaunches = 3;
 
 constexpr uint32_t kPlanMagic = 0x4D4E4250u;  // "PBNM"
