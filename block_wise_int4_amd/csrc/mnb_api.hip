@@ -176,7 +176,7 @@ int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block
         int out = 0, decode_tables = 0;
         // one launch per (kind, variant) present
         for (int kind = kKindGemv; kind <= kKindGemm && st == MNB_OK; ++kind) {
-            for (int v = 0; v < 8 && st == MNB_OK; ++v) {
+            for (int v = 0; v < 16 && st == MNB_OK; ++v) {
                 PlanLaunch L{};
                 L.kind = kind;
                 L.variant = v;

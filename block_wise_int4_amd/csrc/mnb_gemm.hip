@@ -3,33 +3,43 @@
 // buffer-to-LDS loads.
 //
 // Workgroup = WM x WN waves; wave (wm, wn) computes an (MF * 16) x (NF * 16)
-// block of Y, so the workgroup tile is (WM * MF * 16) x (WN * NF * 16).
+// block of Y, so the workgroup tile is (WM * MF * 16) x (WN * NF * 16). The
+// large-M tiles are 208 (or 192) rows by 256 columns, 8 waves of 208 x 32:
+// the accumulators (104 registers) leave room for two waves per SIMD, so one
+// wave's MFMAs overlap the other's loads and dequantization.
 //
 // Weight side: a wave owns NF 16-row groups of W (= NF 16-column fragments
 // of Y). For each 128-input tile it issues one coalesced 128-bit load per
-// lane and fragment (lane l holds row l & 15, chunk l >> 4: 32 codes), forms
-// exact (q - zp) float16 pairs with the 1024-offset trick and multiplies by
-// the block scale with one rounding (the same helper as mnb_dequant, so the
-// MFMA operands are exactly the dequantized weights). Those 32 values are
-// the lane's B operands for the four MFMAs of the tile: MFMA t uses inputs
-// t*8 .. t*8+7 of the lane's chunk. The sum over K does not care which
-// inputs an MFMA groups together as long as A and B agree, so A is laid out
-// with the same grouping and no lane shuffles are needed on either side.
+// lane and fragment (lane l holds row l & 15, chunk l >> 4: 32 codes), plus
+// the block's scale and zero point. MFMA k-slice t (t = 0..3) uses inputs
+// t*8 .. t*8+7 of the lane's chunk: the lane turns that word into exact
+// (q - zp) float16 pairs with the 1024-offset trick and multiplies them by
+// the scale with one rounding (the helper mnb_dequant uses, so the MFMA
+// operands are exactly the dequantized weights). The sum over K does not
+// care which inputs an MFMA groups together as long as A and B agree, so A
+// is laid out with the same grouping and no lane shuffles are needed on
+// either side. Two operand slots alternate: slice t is multiplied from one
+// while slice t + 1 is dequantized into the other.
 //
 // Activation side: the 128-input tile is split in two LDS stages of 64
-// inputs (stage h feeds MFMAs t = 2h, 2h+1). A stage is a list of 1 KB
-// lines, one per (16-row fragment, t): line byte 16*l holds the 8 inputs
-// lane l passes to that MFMA, so every A read is one conflict-free
+// inputs (stage h feeds slices t = 2h, 2h+1). A stage is a list of 1 KB
+// lines, one per (16-row fragment, slice): byte 16*l of a line holds the 8
+// inputs lane l passes to that MFMA, so every A read is one conflict-free
 // ds_read_b128 of a contiguous kilobyte. The lines are filled by
 // buffer_load_dwordx4 ... lds, whose 64 lanes write 64 consecutive 16-byte
-// slots: each lane simply loads the piece its slot needs. Rows past M and
-// inputs past K fall outside the buffer's range and read as zero. Stages are
-// double buffered with one barrier per stage.
+// slots: each lane loads the piece its slot needs. Rows past M and inputs
+// past K fall outside the buffer's range and read as zero. Three stage
+// buffers (two where they do not fit) let the loads run two stages ahead,
+// with one barrier per stage.
 #include "mnb_internal.h"
 
 namespace mnb {
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+#ifndef MNB_GEMM_SCHED
+#define MNB_GEMM_SCHED 5  // A-fragment reads kept ahead of the MFMAs (0: compiler's order)
+#endif
 
 template <int MF, int NF, int WM, int WN>
 struct GemmCfg {
@@ -37,7 +47,7 @@ struct GemmCfg {
     static constexpr int kNT = WN * NF * 16;
     static constexpr int kWaves = WM * WN;
     static constexpr int kThreads = 64 * kWaves;
-    static constexpr int kLines = WM * MF * 2;                       // 1 KB lines per stage
+    static constexpr int kLines = WM * MF * 2;  // 1 KB lines per stage
     static constexpr int kLinesPerWave = (kLines + kWaves - 1) / kWaves;
     static constexpr int kStageBytes = kLines * 1024;
     // as many stage buffers as fit in the CU's 160 KB (at most 3)
@@ -45,6 +55,16 @@ struct GemmCfg {
 };
 
 constexpr uint32_t kOob = 0x7FFFFFF0u;  // a buffer offset past any range we build
+
+// A value made wave-uniform (kept in a scalar register, so branches on it
+// stay scalar branches).
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_readfirstlane(v);
+#else
+    return v;
+#endif
+}
 
 // Workgroups are handed to the 8 XCDs round-robin (block b runs on XCD b % 8),
 // and each XCD has its own L2. Renumbering so that XCD x runs a contiguous
@@ -61,14 +81,16 @@ __device__ __forceinline__ int64_t xcd_logical_wg(int64_t b, int64_t n) {
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
+#if defined(__HIP_DEVICE_COMPILE__)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+#endif
 }
 
 template <int NF>
 struct BRaw {
     u32x4 codes[NF];
-    u32x4 smeta[NF];    // float16 scales of 8 consecutive tiles
-    uint32_t zmeta[NF]; // zero points of the same 8 tiles
+    uint32_t s[NF];  // float16 scale bits of the lane's block
+    uint32_t z[NF];  // its zero point (low nibble)
 };
 
 template <int MF, int NF, int WM, int WN>
@@ -79,7 +101,8 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     const int64_t m0 = tm * C::kMT;
     const int64_t g0 = tn * (WN * NF);
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = (int)uniform_u32((uint32_t)tid >> 6);
+    const int lane = tid & 63;
     const int wm = wave / WN, wn = wave % WN;
     const int r = lane & 15, j = lane >> 4;
     const int e = (j / (p.bs / kChunk)) * kTileRows + r;
@@ -101,7 +124,7 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
         const int64_t c = stage >> 1;
         const int h = (int)(stage & 1);
         const uint32_t soff = (uint32_t)((c * kTileK + h * 16) * 2);
-        uint8_t *buf = lds + (int)(stage % C::kBufs) * C::kStageBytes;
+        uint8_t *buf = lds + (int)((uint32_t)stage % (uint32_t)C::kBufs) * C::kStageBytes;
         const bool last = k_tail && c == p.kg - 1;
 #pragma unroll
         for (int i = 0; i < C::kLinesPerWave; ++i) {
@@ -121,41 +144,33 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
             const int64_t g = g0 + wn * NF + b;
             if (g < p.rg) {
                 R.codes[b] = *(reinterpret_cast<const u32x4 *>(p.packed + (g * p.kg + c) * kTileCodeBytes) + lane);
-                if ((c & (kMetaGroup - 1)) == 0) {
-                    const int64_t mi = meta_index(g, p.nbt, p.kgp, e, c);
-                    R.smeta[b] = *reinterpret_cast<const u32x4 *>(p.packed + p.scales_off + mi * 2);
-                    R.zmeta[b] = *reinterpret_cast<const uint32_t *>(p.packed + p.zp_off + (mi >> 1));
-                }
+                const int64_t mi = meta_index(g, p.nbt, p.kgp, e, c);
+                R.s[b] = *reinterpret_cast<const uint16_t *>(p.packed + p.scales_off + mi * 2);
+                R.z[b] = (uint32_t)p.packed[p.zp_off + (mi >> 1)] >> (4 * (mi & 1));
             } else {
                 R.codes[b] = u32x4{0u, 0u, 0u, 0u};
-                R.smeta[b] = u32x4{0u, 0u, 0u, 0u};
-                R.zmeta[b] = 0u;
+                R.s[b] = 0u;
+                R.z[b] = 0u;
             }
         }
     };
-    // dequantize MFMA operands t = 2h, 2h+1 of tile c into out[b][0..1]
-    auto dequant_half = [&](int64_t c, int h, const BRaw<NF> &R, h8 (&out)[NF][2]) {
-        const int u = (int)(c & (kMetaGroup - 1));
+    // B operands of slice t (inputs t*8 .. t*8+7 of the lane's chunk)
+    auto dequant_t = [&](const BRaw<NF> &R, int t, h8 (&out)[NF]) {
 #pragma unroll
         for (int b = 0; b < NF; ++b) {
-            const u32x4 sm = R.smeta[b];
-            const uint32_t sw = sm[u >> 1];
-            const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)(sw >> (16 * (u & 1))));
-            const h2 zm = zp_magic((R.zmeta[b] >> (4 * u)) & 15u);
+            const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)R.s[b]);
+            const h2 zm = zp_magic(R.z[b] & 15u);
             const h2 s2 = {s, s};
             const u32x4 w = R.codes[b];
+            const uint32_t word = w[t];
+            h8 v;
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const uint32_t word = w[2 * h + tt];
-                h8 v;
-#pragma unroll
-                for (int hh = 0; hh < 4; ++hh) {
-                    const h2 d = dequant_pair_f16(word, hh, zm, s2);
-                    v[2 * hh] = d.x;
-                    v[2 * hh + 1] = d.y;
-                }
-                out[b][tt] = v;
+            for (int hh = 0; hh < 4; ++hh) {
+                const h2 d = dequant_pair_f16(word, hh, zm, s2);
+                v[2 * hh] = d.x;
+                v[2 * hh + 1] = d.y;
             }
+            out[b] = v;
         }
     };
 
@@ -165,73 +180,101 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
 #pragma unroll
         for (int b = 0; b < NF; ++b) acc[a][b] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto mfma_stage = [&](int64_t stage, const h8 (&bw)[NF][2]) {
-        const uint8_t *As = lds + (int)(stage % C::kBufs) * C::kStageBytes + (wm * MF * 2) * 1024 + lane * 16;
+    // one slice: each A fragment of the wave (line 2a + tt of the stage)
+    // times the slice's B operands
+    auto phase = [&](int64_t stage, int tt, const h8 (&bw)[NF]) {
+        const uint8_t *As = lds + (int)((uint32_t)stage % (uint32_t)C::kBufs) * C::kStageBytes +
+                            (wm * MF * 2 + tt) * 1024 + lane * 16;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
+        for (int a = 0; a < MF; ++a) {
+            const h8 av = *reinterpret_cast<const h8 *>(As + a * 2048);
 #pragma unroll
-            for (int a = 0; a < MF; ++a) {
-                const h8 av = *reinterpret_cast<const h8 *>(As + (a * 2 + tt) * 1024);
-#pragma unroll
-                for (int b = 0; b < NF; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw[b][tt], acc[a][b], 0, 0, 0);
-            }
+            for (int b = 0; b < NF; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw[b], acc[a][b], 0, 0, 0);
         }
     };
-    // end of a stage: the next stage's lines (issued one stage earlier) must
-    // be in LDS for every wave; the lines two stages ahead may stay in flight
-    auto stage_sync = [&](int64_t stage, int64_t n_stages) {
-        if (C::kBufs == 3 && stage + 2 < n_stages) wait_vmem<C::kLinesPerWave>();
-        else wait_vmem<0>();
-        __syncthreads();
+    // Instruction order of a slice: the fragment reads run MNB_GEMM_SCHED
+    // ahead of the MFMAs that use them, and the next slice's dequant
+    // arithmetic is spread between the MFMA groups.
+    auto schedule_phase = [&]() {
+#if MNB_GEMM_SCHED
+        constexpr int kAhead = MNB_GEMM_SCHED < MF ? MNB_GEMM_SCHED : MF;
+        constexpr int kValu = (NF * 16 + MF - 1) / MF;
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
+            if (i + kAhead < MF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+        }
+#endif
     };
 
     const int64_t n_stages = 2 * p.kg;
-    BRaw<NF> rc, rn;   // raw weights of the current and the next tile
-    h8 bw0[NF][2], bw1[NF][2];
-    load_b(0, rc);
+    // a wave may own one line fewer than kLinesPerWave; it waits for its own count
+    const bool full_lines = wave + (C::kLinesPerWave - 1) * C::kWaves < C::kLines;
+    // the next stage's lines must have landed; those two stages ahead may
+    // still be in flight (each wave waits for its own loads, then the barrier)
+    auto stage_sync = [&](int64_t stage) {
+        if (C::kBufs == 3 && stage + 2 < n_stages) {
+            if (full_lines) wait_vmem<C::kLinesPerWave>();
+            else wait_vmem<C::kLinesPerWave - 1>();
+        } else {
+            wait_vmem<0>();
+        }
+        __syncthreads();
+    };
+    auto issue_ahead = [&](int64_t stage) {
+        if (C::kBufs == 3) {
+            if (stage + 2 < n_stages) issue_a(stage + 2);
+        } else if (stage + 1 < n_stages) {
+            issue_a(stage + 1);
+        }
+    };
+
+    // Tile c: slices 0..3 in two stages. Weights of tile c + 1 are loaded
+    // first, so that at each stage end only the newest lines may be pending.
+    h8 s0[NF], s1[NF];
+    auto tile = [&](int64_t c, const BRaw<NF> &Rc, BRaw<NF> &Rn) {
+        const bool more = c + 1 < p.kg;
+        if (more) load_b(c + 1, Rn);
+        issue_ahead(2 * c);
+        phase(2 * c, 0, s0);
+        dequant_t(Rc, 1, s1);
+        schedule_phase();
+        phase(2 * c, 1, s1);
+        dequant_t(Rc, 2, s0);
+        schedule_phase();
+        stage_sync(2 * c);
+        issue_ahead(2 * c + 1);
+        phase(2 * c + 1, 0, s0);
+        dequant_t(Rc, 3, s1);
+        schedule_phase();
+        phase(2 * c + 1, 1, s1);
+        if (more) dequant_t(Rn, 0, s0);
+        schedule_phase();
+        stage_sync(2 * c + 1);
+    };
+
+    BRaw<NF> R0, R1;
+    load_b(0, R0);
     issue_a(0);
     if (C::kBufs == 3 && n_stages > 1) issue_a(1);
-    dequant_half(0, 0, rc, bw0);
-    if (C::kBufs == 3 && n_stages > 1) wait_vmem<C::kLinesPerWave>();
-    else wait_vmem<0>();
+    dequant_t(R0, 0, s0);
+    if (C::kBufs == 3 && n_stages > 1) {
+        if (full_lines) wait_vmem<C::kLinesPerWave>();
+        else wait_vmem<C::kLinesPerWave - 1>();
+    } else {
+        wait_vmem<0>();
+    }
     __syncthreads();
 
-    for (int64_t c = 0; c < p.kg; ++c) {
-        // stage 2c: MFMAs on bw0 (t = 0, 1); meanwhile prepare t = 2, 3
-        {
-            const int64_t s = 2 * c;
-            // weights first: at the stage end everything issued before the
-            // lines two stages ahead must have landed
-            if (c + 1 < p.kg) {
-                rn = rc;  // keep the metadata group unless a new one is loaded
-                load_b(c + 1, rn);
-            }
-            if (C::kBufs == 3) {
-                if (s + 2 < n_stages) issue_a(s + 2);
-            } else {
-                issue_a(s + 1);
-            }
-            mfma_stage(s, bw0);
-            dequant_half(c, 1, rc, bw1);
-            stage_sync(s, n_stages);
-        }
-        // stage 2c+1: MFMAs on bw1 (t = 2, 3); meanwhile prepare tile c+1
-        {
-            const int64_t s = 2 * c + 1;
-            if (C::kBufs == 3) {
-                if (s + 2 < n_stages) issue_a(s + 2);
-            } else if (s + 1 < n_stages) {
-                issue_a(s + 1);
-            }
-            mfma_stage(s, bw1);
-            if (c + 1 < p.kg) {
-                dequant_half(c + 1, 0, rn, bw0);
-                rc = rn;
-            }
-            stage_sync(s, n_stages);
-        }
+    int64_t c = 0;
+    for (; c + 2 <= p.kg; c += 2) {
+        tile(c, R0, R1);
+        tile(c + 1, R1, R0);
     }
+    if (c < p.kg) tile(c, R0, R1);
 
     // ---- epilogue: lane holds rows j*4 + i, column r of each fragment ------
     _Float16 *y = static_cast<_Float16 *>(p.y);
@@ -285,24 +328,25 @@ static const VariantInfo kVariants[] = {
     {16, 64},    // 0: MF 1,  NF 1, 1x4 waves
     {32, 64},    // 1: MF 2,  NF 1, 1x4 waves
     {64, 128},   // 2: MF 4,  NF 2, 1x4 waves
-    {128, 128},  // 3: MF 4,  NF 4, 2x2 waves
-    {256, 128},  // 4: MF 8,  NF 4, 2x2 waves
-    {384, 128},  // 5: MF 12, NF 4, 2x2 waves
-    {416, 128},  // 6: MF 13, NF 4, 2x2 waves
+    {208, 256},  // 3: MF 13, NF 2, 1x8 waves
+    {192, 256},  // 4: MF 12, NF 2, 1x8 waves
 };
-constexpr int kNumVariants = 7;
+constexpr int kNumVariants = 5;
 
 int gemm_variant(int64_t m) {
+#ifdef MNB_GEMM_FORCE_VARIANT
+    if (m > 64) return MNB_GEMM_FORCE_VARIANT;
+#endif
     if (m <= 16) return 0;
     if (m <= 32) return 1;
     if (m <= 64) return 2;
-    // fewest padded rows; on a tie the taller tile (less weight dequant work)
+    // the tall tile that pads M with fewer rows (the 208-row one on a tie)
     int best = 3;
     int64_t best_rows = -1;
     for (int v = 3; v < kNumVariants; ++v) {
         const int64_t mt = kVariants[v].mt;
         const int64_t rows = (m + mt - 1) / mt * mt;
-        if (best_rows < 0 || rows <= best_rows) {
+        if (best_rows < 0 || rows < best_rows) {
             best = v;
             best_rows = rows;
         }
@@ -321,10 +365,8 @@ void gemm_tiles(const Problem &p, int variant, int32_t *tiles_m, int32_t *tiles_
     X(0, 1, 1, 1, 4)         \
     X(1, 2, 1, 1, 4)         \
     X(2, 4, 2, 1, 4)         \
-    X(3, 4, 4, 2, 2)         \
-    X(4, 8, 4, 2, 2)         \
-    X(5, 12, 4, 2, 2)        \
-    X(6, 13, 4, 2, 2)
+    X(3, 13, 2, 1, 8)        \
+    X(4, 12, 2, 1, 8)
 
 hipError_t launch_gemm(const Problem &p, int variant, hipStream_t st) {
     const unsigned grid = (unsigned)((int64_t)p.tiles_m * p.tiles_n);
