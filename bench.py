@@ -32,16 +32,20 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
 LLC_BYTES = 256e6              # Infinity Cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ("mnb_gemv.hip", "mnb_gemm.hip", "mnb_device.h", "mnb_layout.h", "mnb_internal.h")
+# sources each measured kernel is built from (counter data is tied to them)
+KERNEL_SOURCES = {
+    "decode_grouped_kernel": ("mnb_gemv.hip", "mnb_device.h", "mnb_layout.h", "mnb_internal.h"),
+    "gemm_grouped_kernel": ("mnb_gemm.hip", "mnb_device.h", "mnb_layout.h", "mnb_internal.h"),
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha():
+def kernel_source_sha(kernel):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "block_wise_int4_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -55,26 +59,86 @@ def stored_traffic(kernel_key):
             rec = json.load(f).get(kernel_key)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha") != kernel_source_sha():
+    if not rec or rec.get("source_sha") != kernel_source_sha(kernel_key.split(":")[0]):
         return None
     return rec.get("bytes_per_launch")
 
 
-def time_steps(fn_list, steps, warmup, torch):
-    """Run fn_list[i % R]() for warmup + steps; time the last `steps` with
-    events on the current stream. Returns ms per step."""
+def record_traffic(fetch_csv, write_csv, probe_mib, workloads, command):
+    """Turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then
+    WRITE_SIZE, both with --copy-probe-mib) into HBM bytes per launch.
+
+    Each counter is scaled by bytes / reading of the plain device copy of
+    probe_mib MiB that the run made (the largest copy dispatch), so that the
+    counters' units and what they count once are calibrated on the same box.
+    Writes profiles/traffic.json and prints a markdown summary."""
+    import csv
+
+    probe = probe_mib << 20
+    per = {}
+    factors = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        if not copies:
+            raise SystemExit(f"{path}: no copy dispatch to calibrate {counter}")
+        factors[counter] = probe / (max(copies) * 1024.0)
+        for kernel in KERNEL_SOURCES:
+            vals = [float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"]]
+            if vals:
+                per.setdefault(kernel, {})[counter] = (sum(vals) / len(vals), len(vals))
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    lines = ["| kernel | workload | FETCH_SIZE KiB/launch | WRITE_SIZE KiB/launch | launches | "
+             "HBM bytes/launch (calibrated) |", "|---|---|---:|---:|---:|---:|"]
+    for kernel, vals in per.items():
+        if "FETCH_SIZE" not in vals or "WRITE_SIZE" not in vals:
+            continue
+        fetch, n = vals["FETCH_SIZE"]
+        write, _ = vals["WRITE_SIZE"]
+        nbytes = int(round(fetch * 1024 * factors["FETCH_SIZE"] + write * 1024 * factors["WRITE_SIZE"]))
+        key = f"{kernel}:{workloads[kernel]}"
+        data[key] = {"bytes_per_launch": nbytes, "fetch_kib": round(fetch, 1), "write_kib": round(write, 1),
+                     "fetch_factor": round(factors["FETCH_SIZE"], 5),
+                     "write_factor": round(factors["WRITE_SIZE"], 5),
+                     "source_sha": kernel_source_sha(kernel), "command": command}
+        lines.append(f"| `{kernel}` | {workloads[kernel]} | {fetch:.1f} | {write:.1f} | {n} | {nbytes} |")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(f"calibration ({probe_mib} MiB copy): FETCH_SIZE x {factors['FETCH_SIZE']:.5f}, "
+          f"WRITE_SIZE x {factors['WRITE_SIZE']:.5f}")
+    print("\n".join(lines))
+
+
+def time_steps(fn_list, steps, warmup, torch, per_launch=False):
+    """Run fn_list[i % R]() for warmup + steps and time the last `steps` with
+    HIP events on the current stream (the stream the kernels run on).
+    Returns (ms per step, list of per-call ms or None). With per_launch, an
+    event pair also brackets every timed call; for a one-launch step that is
+    the kernel's own duration."""
     R = len(fn_list)
     for i in range(warmup):
         fn_list[i % R]()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)] if per_launch else None
     start.record()
     for i in range(steps):
+        if marks:
+            marks[i][0].record()
         fn_list[(warmup + i) % R]()
+        if marks:
+            marks[i][1].record()
     end.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    per = [a.elapsed_time(b) for a, b in marks] if marks else None
+    return start.elapsed_time(end) / steps, per
 
 
 def run_workload(cfg, steps, warmup, per_linear, torch, dev):
@@ -94,10 +158,17 @@ def run_workload(cfg, steps, warmup, per_linear, torch, dev):
     log(f"[bench] {cfg.name}: ready in {time.time() - t0:.1f}s, {replicas} replicas "
         f"({replicas * (weight_bytes + io_bytes) / 1e9:.2f} GB resident)")
 
-    ms = time_steps([lambda p=p: mnb.mnb_gemm_grouped(p) for p in plans], steps, warmup, torch)
-    log(f"[bench] {cfg.name}: grouped {ms * 1e3:.1f} us/step")
-    out = {"ms": ms, "bytes": algo, "flops": flops, "replicas": replicas,
-           "launches_per_step": mnb.mnb_plan_launches(plans[0])}
+    launches = mnb.mnb_plan_launches(plans[0])
+    ms, per = time_steps([lambda p=p: mnb.mnb_gemm_grouped(p) for p in plans], steps, warmup, torch,
+                         per_launch=launches == 1)
+    out = {"ms": ms, "bytes": algo, "flops": flops, "replicas": replicas, "launches_per_step": launches}
+    if per:
+        srt = sorted(per)
+        out["launch_ms"] = sum(per) / len(per)
+        log(f"[bench] {cfg.name}: grouped {ms * 1e3:.1f} us/step; kernel avg {out['launch_ms'] * 1e3:.1f} us "
+            f"(min {srt[0] * 1e3:.1f}, median {srt[len(srt) // 2] * 1e3:.1f}, max {srt[-1] * 1e3:.1f})")
+    else:
+        log(f"[bench] {cfg.name}: grouped {ms * 1e3:.1f} us/step ({launches} launches per step)")
     if per_linear:
         def one_pass(s):
             def f():
@@ -108,7 +179,7 @@ def run_workload(cfg, steps, warmup, per_linear, torch, dev):
                         mnb.mnb_gemm(ld.x, ld.pw, ld.y)
             return f
         pl_steps = max(3, steps // 4)
-        out["per_linear_ms"] = time_steps([one_pass(s) for s in sets], pl_steps, min(warmup, 3), torch)
+        out["per_linear_ms"], _ = time_steps([one_pass(s) for s in sets], pl_steps, min(warmup, 3), torch)
         log(f"[bench] {cfg.name}: per-linear {out['per_linear_ms'] * 1e3:.1f} us/step")
     del plans, sets, base
     torch.cuda.empty_cache()
@@ -152,8 +223,8 @@ def cpu_baseline(cfg, budget_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=1, help="headline workload (index into workloads.configs)")
     ap.add_argument("--prefill-config", type=int, default=3, help="prefill workload timed alongside; -1 = none")
     ap.add_argument("--no-per-linear", action="store_true")
@@ -161,7 +232,17 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per workload")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size (counter calibration runs)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="store HBM bytes per launch from two counter runs (no GPU needed)")
+    ap.add_argument("--traffic-command", default="", help="the profiled command, stored with --record-traffic")
     args = ap.parse_args()
+
+    if args.record_traffic:
+        from workloads import configs
+        wl = {"decode_grouped_kernel": configs.CONFIGS[args.config].name,
+              "gemm_grouped_kernel": configs.CONFIGS[args.prefill_config].name}
+        record_traffic(*args.record_traffic, args.copy_probe_mib or 512, wl, args.traffic_command)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -192,7 +273,9 @@ def main():
     cfg = configs.CONFIGS[args.config]
     dec = run_workload(cfg, args.steps, args.warmup, not args.no_per_linear, torch, dev)
     gbs = dec["bytes"] / (dec["ms"] * 1e-3) / 1e9
-    decode_kernel = "gemv_grouped_f16" if cfg.m == 1 else "gemm_grouped"
+    # one launch per step: the kernel's algorithmic bytes per launch are the step's
+    k_gbs = dec["bytes"] / (dec.get("launch_ms", dec["ms"]) * 1e-3) / 1e9
+    decode_kernel = "decode_grouped_kernel" if cfg.m == 1 else "gemm_grouped_kernel"
     dec_traffic = stored_traffic(f"{decode_kernel}:{cfg.name}")
 
     result = {
@@ -218,26 +301,32 @@ def main():
             if "per_linear_ms" in dec else None,
         },
         "roofline": {
-            "bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(k_gbs / HBM_PEAK_GBS, 4),
             "traffic": dec_traffic,
+            "kernel": decode_kernel, "launch_us": round(dec.get("launch_ms", dec["ms"]) * 1e3, 2),
+            "algorithmic_bytes_per_launch": dec["bytes"],
         },
     }
 
     if args.prefill_config >= 0:
         pcfg = configs.CONFIGS[args.prefill_config]
-        pre = run_workload(pcfg, max(5, args.steps // 2), max(2, args.warmup // 2), not args.no_per_linear,
+        pre = run_workload(pcfg, max(5, args.steps // 10), max(2, args.warmup // 10), not args.no_per_linear,
                            torch, dev)
         tf = pre["flops"] / (pre["ms"] * 1e-3) / 1e12
+        k_tf = pre["flops"] / (pre.get("launch_ms", pre["ms"]) * 1e-3) / 1e12
         result["prefill"] = {
             "workload": pcfg.name, "M": pcfg.m, "linears": len(pcfg.linears), "value": round(tf, 2),
             "unit": "TFLOP/s", "ms_per_step": round(pre["ms"], 5), "schedule": "grouped",
             "launches_per_step": pre["launches_per_step"],
             "per_linear_TFLOPs": round(pre["flops"] / (pre["per_linear_ms"] * 1e-3) / 1e12, 2)
             if "per_linear_ms" in pre else None,
-            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                         "traffic": stored_traffic(f"gemm_grouped:{pcfg.name}")},
+            "roofline": {"bound": "mfma", "achieved": round(k_tf, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(k_tf / MFMA_F16_PEAK_TFLOPS, 4),
+                         "traffic": stored_traffic(f"gemm_grouped_kernel:{pcfg.name}"),
+                         "kernel": "gemm_grouped_kernel",
+                         "launch_us": round(pre.get("launch_ms", pre["ms"]) * 1e3, 2),
+                         "algorithmic_flops_per_launch": pre["flops"]},
         }
 
     if not args.no_cpu_baseline:
