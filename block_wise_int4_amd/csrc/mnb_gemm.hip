@@ -10,8 +10,10 @@
 //
 // Weight side: a wave owns NF 16-row groups of W (= NF 16-column fragments
 // of Y). For each 128-input tile it issues one coalesced 128-bit load per
-// lane and fragment (lane l holds row l & 15, chunk l >> 4: 32 codes), plus
-// the block's scale and zero point. MFMA k-slice t (t = 0..3) uses inputs
+// lane and fragment (lane l holds row l & 15, chunk l >> 4: 32 codes). The
+// scales and zero points of its row groups reach LDS once per 8 tiles by
+// direct buffer-to-LDS loads (one contiguous span per row group and tile
+// group), and each tile's values are read from there. MFMA k-slice t (t = 0..3) uses inputs
 // t*8 .. t*8+7 of the lane's chunk: the lane turns that word into exact
 // (q - zp) float16 pairs with the 1024-offset trick and multiplies them by
 // the scale with one rounding (the helper mnb_dequant uses, so the MFMA
@@ -31,6 +33,10 @@
 // past K fall outside the buffer's range and read as zero. Three stage
 // buffers (two where they do not fit) let the loads run two stages ahead,
 // with one barrier per stage.
+//
+// Epilogue: each wave converts its accumulators to float16 into its own LDS
+// area (rows padded by 16 bytes, so the four rows a store instruction
+// touches fall in different banks) and writes Y back as 16-byte row pieces.
 #include "mnb_internal.h"
 
 namespace mnb {
@@ -50,8 +56,19 @@ struct GemmCfg {
     static constexpr int kLines = WM * MF * 2;  // 1 KB lines per stage
     static constexpr int kLinesPerWave = (kLines + kWaves - 1) / kWaves;
     static constexpr int kStageBytes = kLines * 1024;
-    // as many stage buffers as fit in the CU's 160 KB (at most 3)
-    static constexpr int kBufs = 3 * kStageBytes <= 160 * 1024 ? 3 : 2;
+    // per wave, two tile groups' metadata of its NF row groups: float16
+    // scales (up to 64 entries x 8 tiles = 1 KB) and zero points (256 B)
+    static constexpr int kMetaScaleBytes = 1024, kMetaZpBytes = 256;
+    static constexpr int kMetaBytes = kWaves * 2 * NF * (kMetaScaleBytes + kMetaZpBytes);
+    // as many stage buffers as fit in the CU's 160 KB next to the metadata (at most 3)
+    static constexpr int kBufs = 3 * kStageBytes + kMetaBytes <= 160 * 1024 ? 3 : 2;
+    static constexpr int kMetaOff = kBufs * kStageBytes;
+    // epilogue staging: each wave's (MF * 16) x (NF * 16) float16 block
+    static constexpr int kOutStride = NF * 32 + 16;
+    static constexpr int kOutWaveBytes = MF * 16 * kOutStride;
+    static constexpr int kLdsBytes = kMetaOff + kMetaBytes > kWaves * kOutWaveBytes ? kMetaOff + kMetaBytes
+                                                                                     : kWaves * kOutWaveBytes;
+    static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
 constexpr uint32_t kOob = 0x7FFFFFF0u;  // a buffer offset past any range we build
@@ -137,16 +154,41 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
         }
     };
 
+    // ---- weight metadata: tile group G of this wave's row groups -> LDS ----
+    const int E = p.nbt * kTileRows;  // metadata entries per tile
+    uint8_t *meta_lds = lds + C::kMetaOff + wave * (2 * NF * (C::kMetaScaleBytes + C::kMetaZpBytes));
+    auto meta_s = [&](int slot, int b) { return meta_lds + (slot * NF + b) * C::kMetaScaleBytes; };
+    auto meta_z = [&](int slot, int b) {
+        return meta_lds + 2 * NF * C::kMetaScaleBytes + (slot * NF + b) * C::kMetaZpBytes;
+    };
+    auto issue_meta = [&](int64_t G) {
+        const int slot = (int)(G & 1);
+#pragma unroll
+        for (int b = 0; b < NF; ++b) {
+            const int64_t g = g0 + wn * NF + b;
+            if (g < p.rg) {
+                const int64_t mi = meta_index(g, p.nbt, p.kgp, 0, G * kMetaGroup);
+                const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<uint8_t *>(p.packed + p.scales_off + mi * 2), 0, E * kMetaGroup * 2, 0x00020000);
+                const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<uint8_t *>(p.packed + p.zp_off + mi / 2), 0, E * kMetaGroup / 2, 0x00020000);
+                const uint32_t so = (uint32_t)lane * 16u, zo = (uint32_t)lane * 4u;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void *)meta_s(slot, b), 16, so, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(zr, (lds_void *)meta_z(slot, b), 4, zo, 0, 0, 0);
+            }
+        }
+    };
+
     // ---- weight tiles -------------------------------------------------------
     auto load_b = [&](int64_t c, BRaw<NF> &R) {
+        const int slot = (int)((c / kMetaGroup) & 1), u = (int)(c % kMetaGroup);
 #pragma unroll
         for (int b = 0; b < NF; ++b) {
             const int64_t g = g0 + wn * NF + b;
             if (g < p.rg) {
                 R.codes[b] = *(reinterpret_cast<const u32x4 *>(p.packed + (g * p.kg + c) * kTileCodeBytes) + lane);
-                const int64_t mi = meta_index(g, p.nbt, p.kgp, e, c);
-                R.s[b] = *reinterpret_cast<const uint16_t *>(p.packed + p.scales_off + mi * 2);
-                R.z[b] = (uint32_t)p.packed[p.zp_off + (mi >> 1)] >> (4 * (mi & 1));
+                R.s[b] = *reinterpret_cast<const uint16_t *>(meta_s(slot, b) + e * 16 + u * 2);
+                R.z[b] = (uint32_t)meta_z(slot, b)[e * 4 + (u >> 1)] >> (4 * (u & 1));
             } else {
                 R.codes[b] = u32x4{0u, 0u, 0u, 0u};
                 R.s[b] = 0u;
@@ -235,8 +277,11 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     // Tile c: slices 0..3 in two stages. Weights of tile c + 1 are loaded
     // first, so that at each stage end only the newest lines may be pending.
     h8 s0[NF], s1[NF];
+    const int64_t n_groups = (p.kg + kMetaGroup - 1) / kMetaGroup;
     auto tile = [&](int64_t c, const BRaw<NF> &Rc, BRaw<NF> &Rn) {
         const bool more = c + 1 < p.kg;
+        // the next tile group's metadata, into the slot group c / 8 - 1 used
+        if (c % kMetaGroup == 0 && c / kMetaGroup + 1 < n_groups) issue_meta(c / kMetaGroup + 1);
         if (more) load_b(c + 1, Rn);
         issue_ahead(2 * c);
         phase(2 * c, 0, s0);
@@ -257,9 +302,12 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     };
 
     BRaw<NF> R0, R1;
-    load_b(0, R0);
+    issue_meta(0);
     issue_a(0);
     if (C::kBufs == 3 && n_stages > 1) issue_a(1);
+    // tile group 0's metadata has landed once at most the lines are pending
+    wait_vmem<(C::kBufs == 3 ? 2 : 1) * (C::kLinesPerWave - 1)>();
+    load_b(0, R0);
     dequant_t(R0, 0, s0);
     if (C::kBufs == 3 && n_stages > 1) {
         if (full_lines) wait_vmem<C::kLinesPerWave>();
@@ -277,16 +325,46 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     if (c < p.kg) tile(c, R0, R1);
 
     // ---- epilogue: lane holds rows j*4 + i, column r of each fragment ------
+    // (every wave is past the last barrier, so the stage buffers and the
+    // metadata area are free)
     _Float16 *y = static_cast<_Float16 *>(p.y);
+    const int64_t n_base = (g0 + wn * NF) * kTileRows;
+    const int64_t m_base = m0 + wm * MF * 16;
+    if (p.n % 8 == 0) {
+        uint8_t *ob = lds + wave * C::kOutWaveBytes;
+#pragma unroll
+        for (int a = 0; a < MF; ++a)
+#pragma unroll
+            for (int b = 0; b < NF; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<_Float16 *>(ob + (a * 16 + j * 4 + i) * C::kOutStride + (b * 16 + r) * 2) =
+                        (_Float16)acc[a][b][i];
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        // 16-byte pieces: row q / (2 NF), columns (q % (2 NF)) * 8 .. + 7
+        constexpr int kPieces = MF * 16 * NF * 2;
+#pragma unroll
+        for (int q0 = 0; q0 < kPieces; q0 += 64) {
+            const int q = q0 + lane;
+            if (kPieces % 64 == 0 || q < kPieces) {
+                const int row = q / (NF * 2), piece = q % (NF * 2);
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(ob + row * C::kOutStride + piece * 16);
+                const int64_t m = m_base + row, n = n_base + piece * 8;
+                if (m < p.m && n < p.n) *reinterpret_cast<u32x4 *>(y + m * p.n + n) = v;
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int b = 0; b < NF; ++b) {
-        const int64_t n = (g0 + wn * NF + b) * kTileRows + r;
+        const int64_t n = n_base + b * kTileRows + r;
         if (n >= p.n) continue;
 #pragma unroll
         for (int a = 0; a < MF; ++a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int64_t m = m0 + wm * MF * 16 + a * 16 + j * 4 + i;
+                const int64_t m = m_base + a * 16 + j * 4 + i;
                 if (m < p.m) y[m * p.n + n] = (_Float16)acc[a][b][i];
             }
         }
@@ -295,7 +373,7 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
 
 template <int MF, int NF, int WM, int WN>
 __global__ __launch_bounds__(64 * WM *WN) void gemm_kernel(Problem p) {
-    __shared__ __align__(1024) uint8_t lds[GemmCfg<MF, NF, WM, WN>::kBufs * GemmCfg<MF, NF, WM, WN>::kStageBytes];
+    __shared__ __align__(1024) uint8_t lds[GemmCfg<MF, NF, WM, WN>::kLdsBytes];
     gemm_workgroup<MF, NF, WM, WN>(p, xcd_logical_wg(blockIdx.x, gridDim.x), lds);
 }
 
@@ -311,7 +389,7 @@ __device__ __forceinline__ int find_gemm_problem(const Problem *entries, int cou
 
 template <int MF, int NF, int WM, int WN>
 __global__ __launch_bounds__(64 * WM *WN) void gemm_grouped_kernel(const Problem *entries, int count) {
-    __shared__ __align__(1024) uint8_t lds[GemmCfg<MF, NF, WM, WN>::kBufs * GemmCfg<MF, NF, WM, WN>::kStageBytes];
+    __shared__ __align__(1024) uint8_t lds[GemmCfg<MF, NF, WM, WN>::kLdsBytes];
     const int64_t wg = xcd_logical_wg(blockIdx.x, gridDim.x);
     const int i = find_gemm_problem(entries, count, wg);
     const Problem p = entries[i];

@@ -15,12 +15,14 @@
 //
 // Scales and zero points. Within a tile, row r has nbt = 128 / block_size
 // blocks; entry e = jb * 16 + r names block jb of row r (lane l reads entry
-// (j / (block_size / 32)) * 16 + r). For each row group the metadata is
-// stored entry-major: entry e holds the values of that entry for every tile
-// of the row group, in tile order, padded to kgp = kg rounded up to 8. A lane
-// therefore reads the scales of 8 consecutive tiles with one 16-byte load
-// (float16) and their zero points with one 4-byte load. Zero points are
-// 4-bit, two per byte, even tile in the low nibble.
+// (j / (block_size / 32)) * 16 + r). Tiles are taken in groups of 8 (kgp =
+// kg rounded up to 8), and for each (row group, tile group) the metadata is
+// one contiguous block, entry-major: entry e holds its 8 tiles' values in
+// tile order. A lane therefore reads the scales of 8 consecutive tiles with
+// one 16-byte load (float16) and their zero points with one 4-byte load, and
+// a whole wave reads a tile group's metadata as one contiguous span (1 KB of
+// float16 scales for block 32). Zero points are 4-bit, two per byte, even
+// tile in the low nibble.
 //
 // Rows are padded to a multiple of 16 and inputs to a multiple of 128 with
 // zero codes, zero scales and zero zero-points, which dequantize to exact
@@ -75,9 +77,9 @@ MNB_HD Layout make_layout(int64_t n, int64_t k, int bs, int scale_bytes) {
 }
 
 // Metadata index (in elements for scales, in nibbles for zero points) of
-// entry e of row group g, tile c.
+// entry e of row group g, tile c: block (g, c / 8) of nbt * 16 entries of 8.
 MNB_HD int64_t meta_index(int64_t g, int nbt, int64_t kgp, int e, int64_t c) {
-    return (g * (nbt * kTileRows) + e) * kgp + c;
+    return ((g * (kgp / kMetaGroup) + c / kMetaGroup) * (nbt * kTileRows) + e) * kMetaGroup + c % kMetaGroup;
 }
 
 }  // namespace mnb
