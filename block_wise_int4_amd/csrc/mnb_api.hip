@@ -2,6 +2,7 @@
 // status mapping. Nothing here allocates or synchronizes.
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 
 #include "../../include/mnb.h"
@@ -151,10 +152,12 @@ int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block
     Problem *tmp = new (std::nothrow) Problem[count];
     int *kinds = new (std::nothrow) int[count];
     int *variants = new (std::nothrow) int[count];
-    if (!tmp || !kinds || !variants) {
+    int *order = new (std::nothrow) int[count];
+    if (!tmp || !kinds || !variants || !order) {
         delete[] tmp;
         delete[] kinds;
         delete[] variants;
+        delete[] order;
         return MNB_ERR_INVALID;
     }
     for (int i = 0; i < count && st == MNB_OK; ++i) {
@@ -183,8 +186,11 @@ int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block
                 L.first = out;
                 int64_t wgs = 0;
                 size_t lds = 0;
-                for (int i = 0; i < count; ++i) {
-                    if (kinds[i] != kind || variants[i] != v) continue;
+                int n_sel = 0;
+                for (int i = 0; i < count; ++i)
+                    if (kinds[i] == kind && variants[i] == v) order[n_sel++] = i;
+                for (int s = 0; s < n_sel; ++s) {
+                    const int i = order[s];
                     Problem p = tmp[i];
                     p.variant = v;
                     p.wg_begin = wgs;
@@ -195,6 +201,13 @@ int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block
                 }
                 L.count = out - L.first;
                 if (L.count == 0) continue;
+                if (kind == kKindGemm) {
+                    if (wgs > 0x7FFFFFFFLL) {
+                        st = MNB_ERR_PLAN;
+                        break;
+                    }
+                    wgs = gemm_xcd_schedule(entries + L.first, L.count, &L.split);
+                }
                 if (kind == kKindGemv && v < 2) {
                     if (decode_tables >= kGemvMaxLaunches) {
                         st = MNB_ERR_PLAN;
@@ -219,6 +232,7 @@ int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block
     delete[] tmp;
     delete[] kinds;
     delete[] variants;
+    delete[] order;
     return st;
 }
 
@@ -245,7 +259,7 @@ int mnb_gemm_grouped(const void *plan_host, const void *plan_device, void *strea
         if (L.first < 0 || L.count < 1 || L.first + L.count > hdr->count) return MNB_ERR_PLAN;
         hipError_t e;
         if (L.kind == kKindGemm) {
-            e = launch_gemm_grouped(dev + L.first, L.count, L.wgs, L.variant, as_stream(stream));
+            e = launch_gemm_grouped(dev + L.first, L.count, L.split, L.variant, as_stream(stream));
         } else {
             const GemvWg *table = reinterpret_cast<const GemvWg *>(static_cast<const uint8_t *>(plan_device) +
                                                                    L.sched_off);

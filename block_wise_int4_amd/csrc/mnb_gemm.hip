@@ -37,6 +37,9 @@
 // Epilogue: each wave converts its accumulators to float16 into its own LDS
 // area (rows padded by 16 bytes, so the four rows a store instruction
 // touches fall in different banks) and writes Y back as 16-byte row pieces.
+#include <algorithm>
+#include <vector>
+
 #include "mnb_internal.h"
 
 namespace mnb {
@@ -87,7 +90,7 @@ __device__ __forceinline__ uint32_t uniform_u32(uint32_t v) {
 // and each XCD has its own L2. Renumbering so that XCD x runs a contiguous
 // range of logical workgroups puts all N-tiles of one product - which read
 // the same activation rows - on one XCD, where they share its L2.
-constexpr int kXcds = 8;
+constexpr int kXcds = kXcdCount;
 __device__ __forceinline__ int64_t xcd_logical_wg(int64_t b, int64_t n) {
     const int64_t q = n / kXcds, rem = n % kXcds;
     const int64_t x = b % kXcds, i = b / kXcds;
@@ -180,21 +183,33 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     };
 
     // ---- weight tiles -------------------------------------------------------
-    auto load_b = [&](int64_t c, BRaw<NF> &R) {
+    auto load_codes = [&](int64_t c, BRaw<NF> &R) {
+#pragma unroll
+        for (int b = 0; b < NF; ++b) {
+            const int64_t g = g0 + wn * NF + b;
+            if (g < p.rg)
+                R.codes[b] = *(reinterpret_cast<const u32x4 *>(p.packed + (g * p.kg + c) * kTileCodeBytes) + lane);
+            else
+                R.codes[b] = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto read_meta = [&](int64_t c, BRaw<NF> &R) {
         const int slot = (int)((c / kMetaGroup) & 1), u = (int)(c % kMetaGroup);
 #pragma unroll
         for (int b = 0; b < NF; ++b) {
             const int64_t g = g0 + wn * NF + b;
             if (g < p.rg) {
-                R.codes[b] = *(reinterpret_cast<const u32x4 *>(p.packed + (g * p.kg + c) * kTileCodeBytes) + lane);
                 R.s[b] = *reinterpret_cast<const uint16_t *>(meta_s(slot, b) + e * 16 + u * 2);
                 R.z[b] = (uint32_t)meta_z(slot, b)[e * 4 + (u >> 1)] >> (4 * (u & 1));
             } else {
-                R.codes[b] = u32x4{0u, 0u, 0u, 0u};
                 R.s[b] = 0u;
                 R.z[b] = 0u;
             }
         }
+    };
+    auto load_b = [&](int64_t c, BRaw<NF> &R) {
+        load_codes(c, R);
+        read_meta(c, R);
     };
     // B operands of slice t (inputs t*8 .. t*8+7 of the lane's chunk)
     auto dequant_t = [&](const BRaw<NF> &R, int t, h8 (&out)[NF]) {
@@ -302,12 +317,15 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     };
 
     BRaw<NF> R0, R1;
+    // metadata, codes and lines of the first K-tile all in flight at once
     issue_meta(0);
+    load_codes(0, R0);
     issue_a(0);
     if (C::kBufs == 3 && n_stages > 1) issue_a(1);
-    // tile group 0's metadata has landed once at most the lines are pending
-    wait_vmem<(C::kBufs == 3 ? 2 : 1) * (C::kLinesPerWave - 1)>();
-    load_b(0, R0);
+    // tile group 0's metadata has landed once at most one code load and the
+    // lines are pending (a wave with metadata issued a code load after it)
+    wait_vmem<1 + (C::kBufs == 3 ? 2 : 1) * (C::kLinesPerWave - 1)>();
+    read_meta(0, R0);
     dequant_t(R0, 0, s0);
     if (C::kBufs == 3 && n_stages > 1) {
         if (full_lines) wait_vmem<C::kLinesPerWave>();
@@ -387,10 +405,16 @@ __device__ __forceinline__ int find_gemm_problem(const Problem *entries, int cou
     return lo;
 }
 
+// Grouped launches: XCD x (blocks b with b % 8 == x) runs its own tile range
+// (whole products, balanced by work on the host, longest K first); blocks
+// past the end of their XCD's range exit at once.
 template <int MF, int NF, int WM, int WN>
-__global__ __launch_bounds__(64 * WM *WN) void gemm_grouped_kernel(const Problem *entries, int count) {
+__global__ __launch_bounds__(64 * WM *WN) void gemm_grouped_kernel(const Problem *entries, int count,
+                                                                   XcdSplit split) {
     __shared__ __align__(1024) uint8_t lds[GemmCfg<MF, NF, WM, WN>::kLdsBytes];
-    const int64_t wg = xcd_logical_wg(blockIdx.x, gridDim.x);
+    const int x = (int)(blockIdx.x % kXcds);
+    const int64_t wg = split.begin[x] + (int64_t)(blockIdx.x / kXcds);
+    if (wg >= split.begin[x + 1]) return;
     const int i = find_gemm_problem(entries, count, wg);
     const Problem p = entries[i];
     gemm_workgroup<MF, NF, WM, WN>(p, wg - p.wg_begin, lds);
@@ -458,10 +482,56 @@ hipError_t launch_gemm(const Problem &p, int variant, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_grouped(const Problem *dev_entries, int count, int64_t wgs, int variant, hipStream_t st) {
+int64_t gemm_xcd_schedule(Problem *entries, int count, XcdSplit *split) {
+    // whole products to XCDs, largest first, each to the least loaded XCD;
+    // a product costs its tiles times (K-tiles + 1)
+    std::vector<int> idx(count), xcd(count);
+    for (int i = 0; i < count; ++i) idx[i] = i;
+    auto cost = [&](int i) { return (int64_t)entries[i].tiles_m * entries[i].tiles_n * (entries[i].kg + 1); };
+    std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return cost(a) > cost(b); });
+    int64_t load[kXcds] = {0};
+    for (int i : idx) {
+        int best = 0;
+        for (int x = 1; x < kXcds; ++x)
+            if (load[x] < load[best]) best = x;
+        xcd[i] = best;
+        load[best] += cost(i);
+    }
+    // entries grouped by XCD; inside a group the products with more K-tiles
+    // come first, so that each XCD ends on short workgroups
+    std::vector<Problem> out;
+    out.reserve(count);
+    int64_t tiles = 0, widest = 0;
+    for (int x = 0; x < kXcds; ++x) {
+        std::vector<int> mine;
+        for (int i = 0; i < count; ++i)
+            if (xcd[i] == x) mine.push_back(i);
+        std::stable_sort(mine.begin(), mine.end(), [&](int a, int b) { return entries[a].kg > entries[b].kg; });
+        split->begin[x] = (int32_t)tiles;
+        const int64_t t0 = tiles;
+        for (int i : mine) {
+            Problem p = entries[i];
+            p.wg_begin = tiles;
+            tiles += (int64_t)p.tiles_m * p.tiles_n;
+            out.push_back(p);
+        }
+        if (tiles - t0 > widest) widest = tiles - t0;
+    }
+    split->begin[kXcds] = (int32_t)tiles;
+    for (int i = 0; i < count; ++i) entries[i] = out[i];
+    return widest * kXcds;
+}
+
+hipError_t launch_gemm_grouped(const Problem *dev_entries, int count, const XcdSplit &split, int variant,
+                               hipStream_t st) {
+    int64_t widest = 0;
+    for (int x = 0; x < kXcds; ++x)
+        if (split.begin[x + 1] - split.begin[x] > widest) widest = split.begin[x + 1] - split.begin[x];
+    const int64_t wgs = widest * kXcds;
     switch (variant) {
 #define X(V, MF, NF, WM, WN) \
-    case V: gemm_grouped_kernel<MF, NF, WM, WN><<<(unsigned)wgs, 64 * WM * WN, 0, st>>>(dev_entries, count); break;
+    case V: gemm_grouped_kernel<MF, NF, WM, WN><<<(unsigned)wgs, 64 * WM * WN, 0, st>>>(dev_entries, count, split); \
+        break;
         MNB_GEMM_VARIANTS(X)
 #undef X
     default: return hipErrorInvalidValue;

@@ -33,6 +33,13 @@ struct Problem {
 // Kernel classes a plan can launch.
 enum Kind : int32_t { kKindGemv = 0, kKindGemm = 1 };
 
+// Prefill launches: the output tiles of XCD x (blocks b with b % 8 == x)
+// are tiles [begin[x], begin[x + 1]) of the launch.
+constexpr int kXcdCount = 8;
+struct XcdSplit {
+    int32_t begin[kXcdCount + 1];
+};
+
 struct PlanLaunch {
     int32_t kind;
     int32_t variant;
@@ -41,6 +48,8 @@ struct PlanLaunch {
     int64_t wgs;             // workgroups of this launch
     int64_t lds;             // dynamic LDS bytes (gemv launches)
     int64_t sched_off;       // decode launches: byte offset of the workgroup table
+    XcdSplit split;          // prefill launches
+    int32_t pad_;
 };
 
 // Decode kernel schedule: workgroup w runs batches [b0, b1) (a batch is 4
@@ -114,6 +123,10 @@ hipError_t launch_gemv_grouped(const Problem *dev_entries, int count, const Gemv
 int gemm_variant(int64_t m);
 void gemm_tiles(const Problem &p, int variant, int32_t *tiles_m, int32_t *tiles_n);
 hipError_t launch_gemm(const Problem &p, int variant, hipStream_t st);
-hipError_t launch_gemm_grouped(const Problem *dev_entries, int count, int64_t wgs, int variant, hipStream_t st);
+hipError_t launch_gemm_grouped(const Problem *dev_entries, int count, const XcdSplit &split, int variant,
+                               hipStream_t st);
+// Host: order and split the problems of one prefill launch across the XCDs
+// (fills wg_begin of each entry); returns the launch's workgroup count.
+int64_t gemm_xcd_schedule(Problem *entries, int count, XcdSplit *split);
 
 }  // namespace mnb

@@ -180,7 +180,7 @@ def test_errors_raise_and_enqueue_nothing():
 # (one grouped plan over the config's linears), checked on sampled rows.
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("ci", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("ci", [0, 1, 2, 3, 4, 5])
 def test_full_size_config_sampled(ci):
     from block_wise_int4_amd import workload
     cfg = configs.CONFIGS[ci]

@@ -396,6 +396,7 @@ def test_audio_token_formula_and_prefill_rows():
     for frames, tokens in _golden("audio_tokens.txt").items():
         assert configs.audio_tokens(int(frames)) == int(tokens)
     assert configs.CONFIGS[3].m == configs.audio_tokens(3000) + 20
+    assert configs.CONFIGS[5].m == configs.audio_tokens(320) + 20
 
 
 # ---------------------------------------------------------------------------

@@ -16,6 +16,10 @@ Linear shapes are (N outputs, K inputs), i.e. W is [N, K] and Y = X @ W^T.
 * Prefill M = 410: audio tokens for 30 s (3000 mel frames) by the formula in
   "Qwen3-ASR-0.6B ONNX for the browser", section "Building the prompt", step
   2, gives 390; plus about 20 prompt rows (steps 3 and 6).
+* Mid-M chunk M = 62: a 3.2 s command gives 42 audio rows by the same
+  formula, plus about 20 prompt rows; the decoder that takes such chunks
+  after a cached prefix is the merged one, quantized at block 64
+  ("qwen3-asr-0.6b-onnx-int4-merged", sections "Why" and "Provenance").
 """
 
 from dataclasses import dataclass, field
@@ -80,6 +84,7 @@ CONFIGS = (
     Config(2, "qwen3-1.7b-decode-step", 1, 32, "f16", _stack(QWEN3_17B_LAYER, 28, 2048)),
     Config(3, "qwen3-1.7b-prefill-m410", 410, 32, "f16", _stack(QWEN3_17B_LAYER, 28)),
     Config(4, "whisper-small-encoder-m1500-bs64", 1500, 64, "f16", _stack(WHISPER_SMALL_LAYER, 12)),
+    Config(5, "qwen3-0.6b-chunk-m62-bs64", 62, 64, "f16", _stack(QWEN3_06B_LAYER, 28)),
 )
 
 PROJ_INDEX = {p: i for i, p in enumerate(
