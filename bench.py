@@ -186,6 +186,42 @@ def run_workload(cfg, steps, warmup, per_linear, torch, dev):
     return out
 
 
+def run_lm_head_argmax(cfg, steps, warmup, torch, dev):
+    """The workload's LM head alone: the fused greedy argmax (no logits
+    written) against the plain decode product (logits written), one launch
+    per step each, rotating over replicas past the last-level cache."""
+    from block_wise_int4_amd import mnb, workload
+
+    lin = [l for l in cfg.linears if l.proj == "lm_head"][0]
+    ld = workload.build_linear(cfg, lin, dev)
+    a = 2 if cfg.dtype == "f16" else 4
+    nb = lin.k // cfg.block_size
+    wbytes = lin.n * lin.k // 2 + lin.n * nb * a + lin.n * ((nb + 1) // 2)
+    reps = max(1, math.ceil(1.1e9 / ld.pw.packed.numel()))
+    pws = [ld.pw] + [mnb.PackedWeight(ld.pw.packed.clone(), ld.pw.N, ld.pw.K, ld.pw.block_size, ld.pw.dtype,
+                                      ld.pw.bits) for _ in range(reps - 1)]
+    x = ld.x.reshape(-1)
+    ws = mnb.argmax_workspace(dev)
+    idx = torch.empty(1, dtype=torch.int64, device=dev)
+    y = torch.empty(lin.n, dtype=ld.y.dtype, device=dev)
+    ms_f, per_f = time_steps([lambda p=p: mnb.mnb_gemv_argmax(x, p, ws, index=idx) for p in pws], steps, warmup,
+                             torch, per_launch=True)
+    ms_g, per_g = time_steps([lambda p=p: mnb.mnb_gemv(x, p, y) for p in pws], steps, warmup, torch,
+                             per_launch=True)
+    kf, kg = sum(per_f) / len(per_f), sum(per_g) / len(per_g)
+    bf = wbytes + lin.k * a + 8
+    bg = wbytes + lin.k * a + lin.n * a
+    log(f"[bench] {cfg.name} LM head {lin.n}x{lin.k}: fused argmax {kf * 1e3:.1f} us, plain {kg * 1e3:.1f} us")
+    del pws
+    torch.cuda.empty_cache()
+    return {"shape": [lin.n, lin.k], "replicas": reps,
+            "fused_argmax": {"kernel_us": round(kf * 1e3, 2), "step_us": round(ms_f * 1e3, 2),
+                             "algorithmic_bytes": bf, "GBps": round(bf / (kf * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(bf / (kf * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "plain_gemv": {"kernel_us": round(kg * 1e3, 2), "step_us": round(ms_g * 1e3, 2),
+                           "algorithmic_bytes": bg, "GBps": round(bg / (kg * 1e-3) / 1e9, 1)}}
+
+
 def cpu_baseline(cfg, budget_s):
     """The oracle (NumPy float64 dequantize + matmul) on the host cores, on a
     bounded prefix of the workload's linears. Quantization is not timed."""
@@ -229,6 +265,7 @@ def main():
     ap.add_argument("--prefill-config", type=int, default=3, help="prefill workload timed alongside; -1 = none")
     ap.add_argument("--no-per-linear", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true", help="skip the LM-head argmax and embedding-gather lines")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per workload")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size (counter calibration runs)")
@@ -308,6 +345,9 @@ def main():
             "algorithmic_bytes_per_launch": dec["bytes"],
         },
     }
+
+    if any(l.proj == "lm_head" for l in cfg.linears) and not args.no_next:
+        result["lm_head_argmax"] = run_lm_head_argmax(cfg, args.steps, args.warmup, torch, dev)
 
     if args.prefill_config >= 0:
         pcfg = configs.CONFIGS[args.prefill_config]

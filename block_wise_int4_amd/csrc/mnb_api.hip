@@ -129,6 +129,19 @@ int mnb_gemm(const void *x, const void *packed, void *y, int64_t M, int64_t N, i
     return hip_status(launch_gemv(p, dtype, variant, as_stream(stream)));
 }
 
+int mnb_gemv_argmax(const void *x, const void *packed, void *y, int64_t *index, void *workspace, int64_t N,
+                    int64_t K, int bits, int block_size, int dtype, void *stream) {
+    if (!index || !workspace) return MNB_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(index) & 7) || !aligned16(workspace)) return MNB_ERR_ALIGN;
+    Problem p;
+    int kind = 0, variant = 0;
+    // y is optional here: validate with x standing in for it
+    int st = prepare_product(x, packed, y ? y : x, 1, N, K, bits, block_size, dtype, &p, &kind, &variant);
+    if (st) return st;
+    p.y = y;
+    return hip_status(launch_gemv_argmax(p, variant, workspace, index, as_stream(stream)));
+}
+
 int mnb_gemv(const void *x, const void *packed, void *y, int64_t N, int64_t K, int bits, int block_size, int dtype,
              void *stream) {
     return mnb_gemm(x, packed, y, 1, N, K, bits, block_size, dtype, stream);

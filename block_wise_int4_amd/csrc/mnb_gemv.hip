@@ -22,6 +22,7 @@
 // - zp * sum_k x_k, with the chunk sum of x read from LDS, and the block
 // scale multiplies the chunk result once. The four chunk lanes of each row
 // are summed with two cross-lane exchanges at the end of the row group.
+#include "../../include/mnb.h"
 #include "mnb_internal.h"
 
 namespace mnb {
@@ -178,10 +179,31 @@ __device__ __forceinline__ void stage_x(const Problem &p, T *xs, float *xsum) {
     __syncthreads();
 }
 
-// Runs batches [b0, b1) starting in problem `pi`.
-template <typename T, bool kGrouped>
-__device__ __forceinline__ void decode_range(const Problem *entries, Problem p, int pi, int64_t b0, int64_t b1,
-                                             uint8_t *smem) {
+// Greedy-argmax key of output n with value v (already rounded to the
+// output dtype): larger key = larger value, equal values = lower index.
+// -0 counts as +0; the values are taken to be finite.
+template <typename T>
+__device__ __forceinline__ uint64_t argmax_key(T v, int64_t n) {
+    uint32_t ord;
+    if constexpr (sizeof(T) == 2) {
+        uint32_t h = __builtin_bit_cast(uint16_t, v);
+        if (h == 0x8000u) h = 0u;
+        ord = (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+    } else {
+        uint32_t u = __builtin_bit_cast(uint32_t, v);
+        if (u == 0x80000000u) u = 0u;
+        ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    }
+    return ((uint64_t)ord << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)n);
+}
+
+// Runs batches [b0, b1) starting in problem `pi`. With kArgmax, y is
+// written only when the problem has one, and the result is the largest
+// argmax key among the outputs this lane finished (0 if none).
+template <typename T, bool kGrouped, bool kArgmax = false>
+__device__ __forceinline__ uint64_t decode_range(const Problem *entries, Problem p, int pi, int64_t b0, int64_t b1,
+                                                 uint8_t *smem) {
+    uint64_t best = 0;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, j = lane >> 4;
     int64_t b = b0;
@@ -220,7 +242,16 @@ __device__ __forceinline__ void decode_range(const Problem *entries, Problem p, 
                 v += __shfl_xor(v, 16);
                 v += __shfl_xor(v, 32);
                 const int64_t n = g * kTileRows + r;
-                if (j == 0 && n < p.n) static_cast<T *>(p.y)[n] = (T)v;
+                if constexpr (kArgmax) {
+                    if (j == 0 && n < p.n) {
+                        const T yv = (T)v;
+                        if (p.y) static_cast<T *>(p.y)[n] = yv;
+                        const uint64_t key = argmax_key<T>(yv, n);
+                        best = key > best ? key : best;
+                    }
+                } else {
+                    if (j == 0 && n < p.n) static_cast<T *>(p.y)[n] = (T)v;
+                }
                 acc = 0.0f;
             }
             if (!nvalid) break;
@@ -231,6 +262,7 @@ __device__ __forceinline__ void decode_range(const Problem *entries, Problem p, 
         }
         b = bend;
     }
+    return best;
 }
 
 #ifndef MNB_DECODE_OCC
@@ -244,6 +276,57 @@ void decode_kernel(Problem p, int64_t wgs) {
     const int64_t nbat = p.batch_end;  // batch_begin = 0 for a single problem
     const int64_t b0 = nbat * blockIdx.x / wgs, b1 = nbat * (blockIdx.x + 1) / wgs;
     decode_range<T, false>(nullptr, p, 0, b0, b1, smem);
+}
+
+// Argmax workspace: one 8-byte slot per workgroup of the product launch.
+static_assert(kGemvMaxWgs * 8 <= MNB_ARGMAX_WORKSPACE_BYTES, "argmax workspace too small");
+
+// Decode product fused with a greedy argmax over its outputs: each
+// workgroup stores the best key of the outputs it produced in its slot.
+template <typename T>
+__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(MNB_DECODE_OCC)))
+void decode_argmax_kernel(Problem p, int64_t wgs, unsigned long long *slots) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ unsigned long long wave_best[kGemvWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t nbat = p.batch_end;
+    const int64_t b0 = nbat * blockIdx.x / wgs, b1 = nbat * (blockIdx.x + 1) / wgs;
+    uint64_t best = decode_range<T, false, true>(nullptr, p, 0, b0, b1, smem);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint64_t o = __shfl_xor(best, off);
+        best = o > best ? o : best;
+    }
+    if (lane == 0) wave_best[wave] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned long long b = wave_best[0];
+#pragma unroll
+        for (int w = 1; w < kGemvWaves; ++w) b = wave_best[w] > b ? wave_best[w] : b;
+        slots[blockIdx.x] = b;
+    }
+}
+
+// Second launch on the same stream (so every slot is visible): the largest
+// key of `count` slots, turned back into its output index.
+__global__ __launch_bounds__(kGemvThreads) void argmax_finish_kernel(const unsigned long long *slots, int count,
+                                                                     int64_t *index) {
+    __shared__ unsigned long long wave_best[kGemvWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    unsigned long long b = 0;
+    for (int w = threadIdx.x; w < count; w += kGemvThreads) b = slots[w] > b ? slots[w] : b;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long o = __shfl_xor(b, off);
+        b = o > b ? o : b;
+    }
+    if (lane == 0) wave_best[wave] = b;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int w = 0; w < kGemvWaves; ++w) b = wave_best[w] > b ? wave_best[w] : b;
+        *index = b == 0 ? -1 : (int64_t)(0xFFFFFFFFu - (uint32_t)b);
+    }
 }
 
 template <typename T>
@@ -441,6 +524,28 @@ hipError_t launch_gemv(const Problem &p0, int dtype, int variant, hipStream_t st
         if ((e = allow_lds(decode_kernel<float>, lds)) != hipSuccess) return e;
         decode_kernel<float><<<(unsigned)wgs, kGemvThreads, lds, st>>>(p, wgs);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_argmax(const Problem &p0, int variant, void *workspace, int64_t *index, hipStream_t st) {
+    const size_t lds = gemv_lds_bytes(p0, variant);
+    Problem p = p0;
+    p.batch_begin = 0;
+    p.batch_end = (p.rg + kGemvWaves - 1) / kGemvWaves;
+    const int64_t wgs = p.batch_end < kGemvMaxWgs ? p.batch_end : kGemvMaxWgs;
+    unsigned long long *slots = static_cast<unsigned long long *>(workspace);
+    hipError_t e = hipSuccess;
+    if (variant == 0) {
+        if ((e = allow_lds(decode_argmax_kernel<_Float16>, lds)) != hipSuccess) return e;
+        decode_argmax_kernel<_Float16><<<(unsigned)wgs, kGemvThreads, lds, st>>>(p, wgs, slots);
+    } else if (variant == 1) {
+        if ((e = allow_lds(decode_argmax_kernel<float>, lds)) != hipSuccess) return e;
+        decode_argmax_kernel<float><<<(unsigned)wgs, kGemvThreads, lds, st>>>(p, wgs, slots);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    argmax_finish_kernel<<<1, kGemvThreads, 0, st>>>(slots, (int)wgs, index);
     return hipGetLastError();
 }
 

@@ -52,6 +52,7 @@ _SIGNATURES = {
     "mnb_unpack": (_int, [_vp, _i64, _i64, _int, _int, _int, _vp, _vp, _vp]),
     "mnb_dequant": (_int, [_vp, _i64, _i64, _int, _int, _int, _vp, _vp]),
     "mnb_gemv": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
+    "mnb_gemv_argmax": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
     "mnb_gemm": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp]),
     "mnb_plan_bytes": (_sz, [_int]),
     "mnb_plan_grouped": (_int, [ctypes.POINTER(mnb_problem), _int, _int, _int, _int, _vp, _sz]),
@@ -206,6 +207,35 @@ def mnb_gemv(x, pw, y=None):
         _dev(x, "x"), _dev(pw.packed, "packed"), _dev(y, "y"), pw.N, pw.K, pw.bits, pw.block_size,
         dtype_code(pw.dtype), _stream(x.device)))
     return y
+
+
+ARGMAX_WORKSPACE_BYTES = 8192
+
+
+def argmax_workspace(device):
+    """A workspace for mnb_gemv_argmax (reusable by calls that run one after
+    another on one stream)."""
+    return torch.empty(ARGMAX_WORKSPACE_BYTES // 8, dtype=torch.int64, device=device)
+
+
+def mnb_gemv_argmax(x, pw, workspace, y=None, index=None, logits=False):
+    """Greedy argmax of y = x @ dequant(W)^T, fused into the decode product.
+    Returns the index as a device int64 tensor of one element (and y, when
+    logits=True or y is given)."""
+    _check_x(x, pw)
+    if x.numel() != pw.K:
+        raise ValueError("mnb_gemv_argmax takes one activation row")
+    if workspace.numel() * workspace.element_size() < ARGMAX_WORKSPACE_BYTES or workspace.device != x.device:
+        raise ValueError("workspace: a device buffer from argmax_workspace()")
+    if y is None and logits:
+        y = torch.empty(pw.N, dtype=pw.dtype, device=x.device)
+    if index is None:
+        index = torch.empty(1, dtype=torch.int64, device=x.device)
+    _check("mnb_gemv_argmax", lib().mnb_gemv_argmax(
+        _dev(x, "x"), _dev(pw.packed, "packed"), None if y is None else _dev(y, "y"), _dev(index, "index"),
+        _dev(workspace, "workspace"), pw.N, pw.K, pw.bits, pw.block_size, dtype_code(pw.dtype),
+        _stream(x.device)))
+    return (index, y) if y is not None else index
 
 
 def mnb_gemm(x, pw, y=None):

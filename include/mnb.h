@@ -142,6 +142,26 @@ int mnb_gemv(const void *x, const void *packed, void *y,
              int64_t N, int64_t K, int bits, int block_size, int dtype, void *stream);
 
 /*
+ * Decode-step product fused with a greedy argmax, for the LM head: the
+ * decoder emits logits for the last position only and decoding picks the
+ * largest one until an end token ("Qwen3-ASR-0.6B ONNX for the browser",
+ * sections "Graph contracts" and "Validation"; "Qwen3-ASR-1.7B ONNX", section
+ * "Inference Pipeline"). Computes the same y as mnb_gemv (rounded to dtype)
+ * and writes to *index (device int64) the n of its largest value, the lowest
+ * such n on ties (-0 counts as +0; y is taken to be finite). y may be NULL:
+ * then the logits are not written at all.
+ *
+ * workspace: device buffer of MNB_ARGMAX_WORKSPACE_BYTES bytes, 16-byte
+ * aligned, any contents: it receives one partial result per workgroup,
+ * which a second launch on the same stream reduces to the index. Calls that
+ * run one after another may share it; calls that may overlap (different
+ * streams) need workspaces of their own. index must be 8-byte aligned.
+ */
+#define MNB_ARGMAX_WORKSPACE_BYTES 8192
+int mnb_gemv_argmax(const void *x, const void *packed, void *y, int64_t *index, void *workspace,
+                    int64_t N, int64_t K, int bits, int block_size, int dtype, void *stream);
+
+/*
  * General product for any M >= 1: Y[M][N] = X[M][K] * D^T, X and Y
  * row-major in dtype. M = 1 runs the decode kernel; float16 with M >= 2
  * runs the matrix-core (MFMA) kernel that dequantizes weight tiles and feeds

@@ -94,6 +94,12 @@ ODD = ctypes.c_void_p((1 << 20) + 8)
     (lambda L: L.mnb_dequant(FAKE, 64, 65, 4, 32, 1, FAKE2, None), SHAPE),
     (lambda L: L.mnb_quantize_rtn(FAKE, 64, 64, 4, 32, 3, FAKE2, FAKE3, FAKE, None), DTYPE),
     (lambda L: L.mnb_quantize_rtn(FAKE, 64, 64, 5, 32, 1, FAKE2, FAKE3, FAKE, None), BITS),
+    (lambda L: L.mnb_gemv_argmax(FAKE, FAKE2, None, None, FAKE3, 64, 64, 4, 32, 1, None), NULL),
+    (lambda L: L.mnb_gemv_argmax(FAKE, FAKE2, None, FAKE3, None, 64, 64, 4, 32, 1, None), NULL),
+    (lambda L: L.mnb_gemv_argmax(FAKE, FAKE2, None, ctypes.c_void_p((3 << 20) + 4), FAKE, 64, 64, 4, 32, 1,
+                                 None), ALIGN),
+    (lambda L: L.mnb_gemv_argmax(FAKE, FAKE2, None, FAKE3, FAKE, 64, 64, 8, 32, 1, None), BITS),
+    (lambda L: L.mnb_gemv_argmax(None, FAKE2, None, FAKE3, FAKE, 64, 64, 4, 32, 1, None), NULL),
 ])
 def test_invalid_arguments_are_rejected_before_launch(L, call, status):
     assert call(L) == status
