@@ -222,6 +222,41 @@ def run_lm_head_argmax(cfg, steps, warmup, torch, dev):
                            "algorithmic_bytes": bg, "GBps": round(bg / (kg * 1e-3) / 1e9, 1)}}
 
 
+def run_embed_gather(cfg, steps, warmup, torch, dev, token_counts=(410, 65536)):
+    """Int8 embedding-row gather for the workload's vocabulary and width,
+    float16 out: a prompt-sized call (410 rows) and a bandwidth-sized one,
+    each rotating over two table copies and eight id sets so that rows come
+    from HBM."""
+    import numpy as np
+
+    from block_wise_int4_amd import mnb
+    from workloads import synth
+
+    lin = [l for l in cfg.linears if l.proj == "lm_head"][0]
+    vocab, hidden = lin.n, lin.k
+    table, scales, _ = synth.embedding_inputs(1, vocab, hidden, 1)
+    tables = [torch.from_numpy(table).to(dev) for _ in range(2)]
+    sc = torch.from_numpy(scales).to(dev)
+    rng = np.random.default_rng(5)
+    res = {"vocab": vocab, "hidden": hidden, "out": "f16"}
+    for tokens in token_counts:
+        id_sets = [torch.from_numpy(rng.integers(0, vocab, size=tokens, dtype=np.int64)).to(dev) for _ in range(8)]
+        out = torch.empty((tokens, hidden), dtype=torch.float16, device=dev)
+        fns = [lambda t=t, i=i: mnb.mnb_embed_gather(t, sc, i, torch.float16, out=out)
+               for i in id_sets for t in tables]
+        ms, per = time_steps(fns, steps, warmup, torch, per_launch=True)
+        k = sum(per) / len(per)
+        nbytes = tokens * hidden + tokens * 4 + tokens * 8 + tokens * hidden * 2
+        log(f"[bench] embedding gather {tokens} x {hidden} of {vocab}: {k * 1e3:.1f} us")
+        res[f"tokens_{tokens}"] = {"kernel_us": round(k * 1e3, 2), "algorithmic_bytes": nbytes,
+                                   "GBps": round(nbytes / (k * 1e-3) / 1e9, 1),
+                                   "frac_hbm": round(nbytes / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del id_sets, out
+    del tables
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cfg, budget_s):
     """The oracle (NumPy float64 dequantize + matmul) on the host cores, on a
     bounded prefix of the workload's linears. Quantization is not timed."""
@@ -348,6 +383,7 @@ def main():
 
     if any(l.proj == "lm_head" for l in cfg.linears) and not args.no_next:
         result["lm_head_argmax"] = run_lm_head_argmax(cfg, args.steps, args.warmup, torch, dev)
+        result["embedding_gather"] = run_embed_gather(cfg, args.steps, args.warmup, torch, dev)
 
     if args.prefill_config >= 0:
         pcfg = configs.CONFIGS[args.prefill_config]

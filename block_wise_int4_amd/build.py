@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmnb.so")
-SOURCES = ("mnb_api.hip", "mnb_aux.hip", "mnb_gemv.hip", "mnb_gemm.hip")
+SOURCES = ("mnb_api.hip", "mnb_aux.hip", "mnb_gemv.hip", "mnb_gemm.hip", "mnb_embed.hip")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

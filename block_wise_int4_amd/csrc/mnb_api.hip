@@ -129,6 +129,18 @@ int mnb_gemm(const void *x, const void *packed, void *y, int64_t M, int64_t N, i
     return hip_status(launch_gemv(p, dtype, variant, as_stream(stream)));
 }
 
+int mnb_embed_gather(const int8_t *table, const float *row_scales, const int64_t *ids, int64_t T, int64_t V,
+                     int64_t H, int dtype, void *out, void *stream) {
+    if (!table || !row_scales || !ids || !out) return MNB_ERR_NULL;
+    if (dtype != MNB_F16 && dtype != MNB_F32) return MNB_ERR_DTYPE;
+    if (T < 0 || V <= 0 || H <= 0 || H % 16 != 0 || T > MNB_MAX_ROWS || V > MNB_MAX_ROWS) return MNB_ERR_SHAPE;
+    if (!aligned16(table) || !aligned16(out) || (reinterpret_cast<uintptr_t>(ids) & 7) ||
+        (reinterpret_cast<uintptr_t>(row_scales) & 3))
+        return MNB_ERR_ALIGN;
+    if (T == 0) return MNB_OK;
+    return hip_status(launch_embed_gather(table, row_scales, ids, T, V, H, dtype, out, as_stream(stream)));
+}
+
 int mnb_gemv_argmax(const void *x, const void *packed, void *y, int64_t *index, void *workspace, int64_t N,
                     int64_t K, int bits, int block_size, int dtype, void *stream) {
     if (!index || !workspace) return MNB_ERR_NULL;

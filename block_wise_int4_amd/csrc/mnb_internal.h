@@ -116,6 +116,9 @@ size_t gemv_lds_bytes(const Problem &p, int variant);
 // each problem and the workgroup table; returns the workgroup count.
 int64_t gemv_schedule(Problem *entries, int count, GemvWg *table, int max_wgs);
 hipError_t launch_gemv(const Problem &p, int dtype, int variant, hipStream_t st);
+// int8 embedding rows times their float32 scale, rounded once to dtype.
+hipError_t launch_embed_gather(const int8_t *table, const float *scales, const int64_t *ids, int64_t rows,
+                               int64_t vocab, int64_t h, int dtype, void *out, hipStream_t st);
 // Decode product (variants 0 and 1) fused with a greedy argmax of y.
 hipError_t launch_gemv_argmax(const Problem &p, int variant, void *workspace, int64_t *index, hipStream_t st);
 hipError_t launch_gemv_grouped(const Problem *dev_entries, int count, const GemvWg *dev_table, int64_t wgs,

@@ -53,6 +53,7 @@ _SIGNATURES = {
     "mnb_dequant": (_int, [_vp, _i64, _i64, _int, _int, _int, _vp, _vp]),
     "mnb_gemv": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
     "mnb_gemv_argmax": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
+    "mnb_embed_gather": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _vp]),
     "mnb_gemm": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp]),
     "mnb_plan_bytes": (_sz, [_int]),
     "mnb_plan_grouped": (_int, [ctypes.POINTER(mnb_problem), _int, _int, _int, _int, _vp, _sz]),
@@ -236,6 +237,25 @@ def mnb_gemv_argmax(x, pw, workspace, y=None, index=None, logits=False):
         _dev(workspace, "workspace"), pw.N, pw.K, pw.bits, pw.block_size, dtype_code(pw.dtype),
         _stream(x.device)))
     return (index, y) if y is not None else index
+
+
+def mnb_embed_gather(table, row_scales, ids, dtype=torch.float16, out=None):
+    """out[t] = table[ids[t]] (int8 [V, H]) * row_scales[ids[t]] (float32 [V]),
+    rounded once to dtype; ids outside [0, V) give zero rows."""
+    if table.dtype != torch.int8 or table.dim() != 2:
+        raise TypeError("table must be int8 [V, H]")
+    if row_scales.dtype != torch.float32 or row_scales.numel() != table.shape[0]:
+        raise TypeError("row_scales must be float32 [V]")
+    if ids.dtype != torch.int64:
+        raise TypeError("ids must be int64")
+    V, H = table.shape
+    T = ids.numel()
+    if out is None:
+        out = torch.empty((T, H), dtype=dtype, device=table.device)
+    _check("mnb_embed_gather", lib().mnb_embed_gather(
+        _dev(table, "table"), _dev(row_scales, "row_scales"), _dev(ids, "ids"), T, V, H, dtype_code(out.dtype),
+        _dev(out, "out"), _stream(table.device)))
+    return out
 
 
 def mnb_gemm(x, pw, y=None):

@@ -162,6 +162,21 @@ int mnb_gemv_argmax(const void *x, const void *packed, void *y, int64_t *index, 
                     int64_t N, int64_t K, int bits, int block_size, int dtype, void *stream);
 
 /*
+ * The step before the product in decode: the next input embeddings, as
+ * int8 rows of the token table times each row's float32 scale ("Qwen3-ASR-
+ * 0.6B ONNX for the browser", section "Building the prompt": an int8 row
+ * times its embed scale, in float32 or float16).
+ *   out[t][h] = table[ids[t]][h] * row_scales[ids[t]], t < T, h < H,
+ * the exact product rounded once (to nearest even) to dtype.
+ * table: device int8 [V][H]; row_scales: device float32 [V]; ids: device
+ * int64 [T]; out: device dtype [T][H]. H must be a positive multiple of 16
+ * (MNB_ERR_SHAPE otherwise); T = 0 enqueues nothing. An id outside [0, V)
+ * gives a row of zeros. Pointers 16-byte aligned (ids: 8).
+ */
+int mnb_embed_gather(const int8_t *table, const float *row_scales, const int64_t *ids, int64_t T, int64_t V,
+                     int64_t H, int dtype, void *out, void *stream);
+
+/*
  * General product for any M >= 1: Y[M][N] = X[M][K] * D^T, X and Y
  * row-major in dtype. M = 1 runs the decode kernel; float16 with M >= 2
  * runs the matrix-core (MFMA) kernel that dequantizes weight tiles and feeds

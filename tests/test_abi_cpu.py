@@ -100,6 +100,12 @@ ODD = ctypes.c_void_p((1 << 20) + 8)
                                  None), ALIGN),
     (lambda L: L.mnb_gemv_argmax(FAKE, FAKE2, None, FAKE3, FAKE, 64, 64, 8, 32, 1, None), BITS),
     (lambda L: L.mnb_gemv_argmax(None, FAKE2, None, FAKE3, FAKE, 64, 64, 4, 32, 1, None), NULL),
+    (lambda L: L.mnb_embed_gather(FAKE, FAKE2, None, 4, 100, 64, 1, FAKE3, None), NULL),
+    (lambda L: L.mnb_embed_gather(FAKE, FAKE2, FAKE, 4, 100, 40, 1, FAKE3, None), SHAPE),
+    (lambda L: L.mnb_embed_gather(FAKE, FAKE2, FAKE, 4, 0, 64, 1, FAKE3, None), SHAPE),
+    (lambda L: L.mnb_embed_gather(FAKE, FAKE2, FAKE, 4, 100, 64, 5, FAKE3, None), DTYPE),
+    (lambda L: L.mnb_embed_gather(FAKE, FAKE2, FAKE, 4, 100, 64, 1, ODD, None), ALIGN),
+    (lambda L: L.mnb_embed_gather(FAKE, FAKE2, FAKE, 0, 100, 64, 1, FAKE3, None), MNB_OK),
 ])
 def test_invalid_arguments_are_rejected_before_launch(L, call, status):
     assert call(L) == status

@@ -61,3 +61,14 @@ def random_case(seed, m, n, k, dtype, weight_std=0.02):
     w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(weight_std)
     x = rng.standard_normal((m, k), dtype=np.float32).astype(np_dtype(dtype))
     return w, x
+
+
+def embedding_inputs(seed, vocab, hidden, tokens):
+    """A synthetic int8 embedding table with per-row float32 scales and token
+    ids: table uniform in [-127, 127], scales |N(0, 0.02)| / 127 (rows of
+    about the spread of the float weights), ids uniform over the vocabulary."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(SEED, spawn_key=(98, seed))))
+    table = rng.integers(-127, 128, size=(vocab, hidden), dtype=np.int8)
+    scales = (np.abs(rng.standard_normal(vocab)) * 0.02 / 127).astype(np.float32)
+    ids = rng.integers(0, vocab, size=tokens, dtype=np.int64)
+    return table, scales, ids
