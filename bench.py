@@ -196,7 +196,7 @@ def run_lm_head_argmax(cfg, steps, warmup, torch, dev):
     ld = workload.build_linear(cfg, lin, dev)
     a = 2 if cfg.dtype == "f16" else 4
     nb = lin.k // cfg.block_size
-    wbytes = lin.n * lin.k // 2 + lin.n * nb * a + lin.n * ((nb + 1) // 2)
+    wbytes = lin.n * lin.k // 2 + lin.n * nb * a + (0 if cfg.symmetric else lin.n * ((nb + 1) // 2))
     reps = max(1, math.ceil(1.1e9 / ld.pw.packed.numel()))
     pws = [ld.pw] + [mnb.PackedWeight(ld.pw.packed.clone(), ld.pw.N, ld.pw.K, ld.pw.block_size, ld.pw.dtype,
                                       ld.pw.bits) for _ in range(reps - 1)]
@@ -276,13 +276,15 @@ def cpu_baseline(cfg, budget_s):
         if lin.proj == "lm_head":
             n_rows = min(lin.n, 16384)   # a slice of the vocabulary keeps the sample bounded
             w = w[:n_rows]
-        q, s, zp = oracle.rtn_quantize(w, cfg.block_size, dt)
+        quantize = oracle.rtn_quantize_symmetric if cfg.symmetric else oracle.rtn_quantize
+        q, s, zp = quantize(w, cfg.block_size, dt)
         t = time.perf_counter()
         oracle.matmul_nbits(x, q, zp, s, cfg.block_size)
         elapsed += time.perf_counter() - t
         nb = lin.k // cfg.block_size
         a = 2 if cfg.dtype == "f16" else 4
-        done_bytes += n_rows * lin.k // 2 + n_rows * nb * a + n_rows * ((nb + 1) // 2) + cfg.m * (lin.k + n_rows) * a
+        zp_bytes = 0 if cfg.symmetric else n_rows * ((nb + 1) // 2)
+        done_bytes += n_rows * lin.k // 2 + n_rows * nb * a + zp_bytes + cfg.m * (lin.k + n_rows) * a
         done_flops += 2 * cfg.m * n_rows * lin.k
         used.append(f"{lin.proj}{'' if lin.layer < 0 else lin.layer}" + ("" if n_rows == lin.n else f"[:{n_rows}]"))
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -365,6 +367,7 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights RTN-quantized on the GPU, N(0,1) activations)",
         "config": {
             "workload": cfg.name, "M": cfg.m, "linears": len(cfg.linears), "block_size": cfg.block_size,
+            "symmetric": cfg.symmetric,
             "activations": cfg.dtype, "accumulate": "f32", "schedule": "grouped",
             "launches_per_step": dec["launches_per_step"], "replicas": dec["replicas"],
             "algorithmic_bytes_per_step": dec["bytes"],

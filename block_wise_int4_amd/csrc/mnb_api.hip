@@ -21,7 +21,7 @@ inline int dtype_bytes(int dtype) { return dtype == MNB_F16 ? 2 : 4; }
 // Format and shape checks common to every entry point.
 int check_format(int64_t n, int64_t k, int bits, int bs, int dtype) {
     if (bits != 4) return MNB_ERR_BITS;
-    if (bs != 32 && bs != 64) return MNB_ERR_BLOCK;
+    if (bs != 32 && bs != 64 && bs != 128) return MNB_ERR_BLOCK;
     if (dtype != MNB_F32 && dtype != MNB_F16) return MNB_ERR_DTYPE;
     if (n <= 0 || k <= 0 || k % bs != 0) return MNB_ERR_SHAPE;
     if (n > MNB_MAX_ROWS || k > MNB_MAX_K) return MNB_ERR_SHAPE;
@@ -64,7 +64,7 @@ const char *mnb_status_string(int status) {
     case MNB_OK: return "ok";
     case MNB_ERR_NULL: return "a required pointer is NULL";
     case MNB_ERR_BITS: return "bits must be 4";
-    case MNB_ERR_BLOCK: return "block_size must be 32 or 64";
+    case MNB_ERR_BLOCK: return "block_size must be 32, 64 or 128";
     case MNB_ERR_SHAPE: return "invalid shape (M, N, K > 0, K a multiple of block_size, within limits)";
     case MNB_ERR_DTYPE: return "unsupported dtype";
     case MNB_ERR_ALIGN: return "device pointer not 16-byte aligned";
@@ -82,16 +82,17 @@ size_t mnb_packed_bytes(int64_t N, int64_t K, int bits, int block_size, int dtyp
 
 int mnb_quantize_rtn(const float *w, int64_t N, int64_t K, int bits, int block_size, int dtype, uint8_t *qweight,
                      void *scales, uint8_t *zero_points, void *stream) {
-    if (!w || !qweight || !scales || !zero_points) return MNB_ERR_NULL;
+    if (!w || !qweight || !scales) return MNB_ERR_NULL;
     int st = check_format(N, K, bits, block_size, dtype);
     if (st) return st;
-    if (!aligned16(w) || !aligned16(qweight) || !aligned16(scales) || !aligned16(zero_points)) return MNB_ERR_ALIGN;
+    if (!aligned16(w) || !aligned16(qweight) || !aligned16(scales) || (zero_points && !aligned16(zero_points)))
+        return MNB_ERR_ALIGN;
     return hip_status(launch_quantize_rtn(w, N, K, block_size, dtype, qweight, scales, zero_points, as_stream(stream)));
 }
 
 int mnb_pack(const uint8_t *qweight, const void *scales, const uint8_t *zero_points, int64_t N, int64_t K, int bits,
              int block_size, int dtype, void *packed, void *stream) {
-    if (!qweight || !scales || !zero_points || !packed) return MNB_ERR_NULL;
+    if (!qweight || !scales || !packed) return MNB_ERR_NULL;
     int st = check_format(N, K, bits, block_size, dtype);
     if (st) return st;
     if (!aligned16(qweight) || !aligned16(packed)) return MNB_ERR_ALIGN;

@@ -7,9 +7,13 @@ namespace mnb {
 
 // ---------------------------------------------------------------------------
 // RTN quantization, one thread per (row, pair of blocks) so that each thread
-// owns whole zero-point bytes. Decisions are taken in float64: the block
-// extent including zero, the scale (hi - lo) / 15 rounded once to the scale
-// dtype, zp = clamp(rint(-lo / s), 0, 15), q = clamp(rint(w / s) + zp, 0, 15).
+// owns whole zero-point bytes. Decisions are taken in float64:
+//  - asymmetric: the block extent including zero, the scale (hi - lo) / 15
+//    rounded once to the scale dtype, zp = clamp(rint(-lo / s), 0, 15);
+//  - symmetric (no zero points written): the scale max|w| / 7 rounded once
+//    to the scale dtype and the fixed zero point 8;
+// then q = clamp(rint(w / s) + zp, 0, 15); a block whose stored scale is 0
+// gets q = zp.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float *__restrict__ w, int64_t n_rows,
@@ -32,16 +36,18 @@ __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float *__restri
             lo = v < lo ? v : lo;
             hi = v > hi ? v : hi;
         }
-        const T stored = Io<T>::round_f64((hi - lo) / 15.0);
+        const bool sym = zps == nullptr;
+        const double amax = -lo > hi ? -lo : hi;
+        const T stored = Io<T>::round_f64(sym ? amax / 7.0 : (hi - lo) / 15.0);
         const double s = (double)stored;
-        uint32_t zp = 0;
-        if (s != 0.0) {
+        uint32_t zp = sym ? 8u : 0u;
+        if (s != 0.0 && !sym) {
             const double z = __builtin_rint(-lo / s);
             zp = (uint32_t)(z < 0.0 ? 0.0 : (z > 15.0 ? 15.0 : z));
         }
         uint8_t *dst = qweight + n * (k / 2) + b * bs / 2;
         for (int i = 0; i < bs; i += 2) {
-            uint32_t c[2] = {0u, 0u};
+            uint32_t c[2] = {zp, zp};
             if (s != 0.0) {
                 for (int t = 0; t < 2; ++t) {
                     const double q = __builtin_rint((double)src[i + t] / s) + (double)zp;
@@ -53,7 +59,7 @@ __global__ __launch_bounds__(256) void quantize_rtn_kernel(const float *__restri
         scales[n * nb + b] = stored;
         zbyte |= zp << (4 * e);
     }
-    zps[n * ((nb + 1) / 2) + p] = (uint8_t)zbyte;
+    if (zps) zps[n * ((nb + 1) / 2) + p] = (uint8_t)zbyte;
 }
 
 // ---------------------------------------------------------------------------
@@ -111,7 +117,8 @@ __global__ __launch_bounds__(256) void pack_meta_kernel(const T *__restrict__ sc
         uint32_t z = 0;
         if (n < L.n && c < L.kg && b < nb) {
             s = scales[n * nb + b];
-            z = (zero_points[n * zpb + b / 2] >> (4 * (b & 1))) & 15u;
+            // no zero points: the symmetric format's fixed 8
+            z = zero_points ? (zero_points[n * zpb + b / 2] >> (4 * (b & 1))) & 15u : 8u;
         }
         sdst[meta_index(g, L.nbt, L.kgp, e, c)] = s;
         zbyte |= z << (4 * h);

@@ -132,8 +132,9 @@ class PackedWeight:
     bits: int = 4
 
 
-def mnb_quantize_rtn(w, block_size, dtype, bits=4, out=None):
-    """RTN-quantize float32 W[N, K] on the GPU -> (qweight, scales, zero_points), canonical layout."""
+def mnb_quantize_rtn(w, block_size, dtype, bits=4, out=None, symmetric=False):
+    """RTN-quantize float32 W[N, K] on the GPU -> (qweight, scales, zero_points),
+    canonical layout; symmetric=True: no zero points (None), fixed zero point 8."""
     if w.dtype != torch.float32 or w.dim() != 2:
         raise ValueError("w must be a 2-D float32 tensor")
     N, K = w.shape
@@ -141,30 +142,32 @@ def mnb_quantize_rtn(w, block_size, dtype, bits=4, out=None):
     if out is None:
         out = (torch.empty((N, K // 2), dtype=torch.uint8, device=w.device),
                torch.empty((N, max(nb, 1)), dtype=dtype, device=w.device),
-               torch.empty((N, max((nb + 1) // 2, 1)), dtype=torch.uint8, device=w.device))
+               None if symmetric else torch.empty((N, max((nb + 1) // 2, 1)), dtype=torch.uint8, device=w.device))
     q, s, z = out
     _check("mnb_quantize_rtn", lib().mnb_quantize_rtn(
         _dev(w, "w"), N, K, bits, block_size, dtype_code(dtype),
-        _dev(q, "qweight"), _dev(s, "scales"), _dev(z, "zero_points"), _stream(w.device)))
+        _dev(q, "qweight"), _dev(s, "scales"), None if z is None else _dev(z, "zero_points"), _stream(w.device)))
     return q, s, z
 
 
 def mnb_pack(qweight, scales, zero_points, N, K, block_size, bits=4, packed=None):
-    """Canonical format -> PackedWeight (device layout of the compute kernels)."""
+    """Canonical format -> PackedWeight (device layout of the compute kernels).
+    zero_points None: the symmetric format (zero point 8 in every block)."""
     dtype = scales.dtype
+    zp_arg = (lambda: None) if zero_points is None else (lambda: _dev(zero_points, "zero_points"))
     nbytes = mnb_packed_bytes(N, K, block_size, dtype, bits)
     if nbytes == 0:
         # invalid format: let the library name the error (it returns before
         # touching the GPU, so a placeholder output address is never used)
         _check("mnb_pack", lib().mnb_pack(
-            _dev(qweight, "qweight"), _dev(scales, "scales"), _dev(zero_points, "zero_points"),
+            _dev(qweight, "qweight"), _dev(scales, "scales"), zp_arg(),
             N, K, bits, block_size, dtype_code(dtype), ctypes.c_void_p(256), None))
     if packed is None:
         packed = torch.empty(nbytes, dtype=torch.uint8, device=qweight.device)
     elif packed.numel() * packed.element_size() < nbytes:
         raise ValueError("packed buffer too small")
     _check("mnb_pack", lib().mnb_pack(
-        _dev(qweight, "qweight"), _dev(scales, "scales"), _dev(zero_points, "zero_points"),
+        _dev(qweight, "qweight"), _dev(scales, "scales"), zp_arg(),
         N, K, bits, block_size, dtype_code(dtype), _dev(packed, "packed"), _stream(qweight.device)))
     return PackedWeight(packed, N, K, block_size, dtype, bits)
 

@@ -46,7 +46,7 @@ def build_linear(cfg, lin, device, m=None, keep_canonical=False, sample_rows=0, 
     w, x = synth.linear_inputs(cfg, lin, m)
     dt = torch_dtype(cfg.dtype)
     wd = torch.from_numpy(w).to(device)
-    q, s, z = mnb.mnb_quantize_rtn(wd, cfg.block_size, dt)
+    q, s, z = mnb.mnb_quantize_rtn(wd, cfg.block_size, dt, symmetric=cfg.symmetric)
     pw = mnb.mnb_pack(q, s, z, lin.n, lin.k, cfg.block_size)
     xd = torch.from_numpy(x).to(device)
     y = torch.empty((x.shape[0], lin.n), dtype=dt, device=device)
@@ -59,7 +59,7 @@ def build_linear(cfg, lin, device, m=None, keep_canonical=False, sample_rows=0, 
         ld.sample_rows = rows
         ld.w_rows = w[rows].copy()
         ld.canonical = (q[rows.tolist()].cpu().numpy(), s[rows.tolist()].cpu().numpy(),
-                        z[rows.tolist()].cpu().numpy())
+                        None if z is None else z[rows.tolist()].cpu().numpy())
     del wd
     return ld
 
@@ -87,13 +87,14 @@ def replicate(cfg, linears):
 
 def algorithmic_bytes(cfg, linears=None):
     """Bytes the method must move per step: codes + scales + packed zero
-    points + activations + outputs, each counted once."""
+    points (none in the symmetric format) + activations + outputs, each
+    counted once."""
     linears = cfg.linears if linears is None else linears
     a = 2 if cfg.dtype == "f16" else 4
     total = 0
     for lin in linears:
         nb = lin.k // cfg.block_size
-        total += lin.n * lin.k // 2 + lin.n * nb * a + lin.n * ((nb + 1) // 2)
+        total += lin.n * lin.k // 2 + lin.n * nb * a + (0 if cfg.symmetric else lin.n * ((nb + 1) // 2))
         total += cfg.m * lin.k * a + cfg.m * lin.n * a
     return total
 

@@ -24,7 +24,7 @@
  *    are reentrant. Calls on one stream run in order.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call that touches device memory is asynchronous on it.
- *  - bits must be 4, block_size 32 or 64, K a positive multiple of
+ *  - bits must be 4, block_size 32, 64 or 128, K a positive multiple of
  *    block_size, M and N positive.
  *  - dtype is the activation dtype, which is also the scale dtype and the
  *    output dtype: MNB_F32 or MNB_F16. Accumulation is float32.
@@ -66,7 +66,7 @@ typedef enum mnb_status {
     MNB_OK = 0,
     MNB_ERR_NULL = 1,      /* a required pointer is NULL                     */
     MNB_ERR_BITS = 2,      /* bits != 4                                      */
-    MNB_ERR_BLOCK = 3,     /* block_size not 32 or 64                        */
+    MNB_ERR_BLOCK = 3,     /* block_size not 32, 64 or 128                   */
     MNB_ERR_SHAPE = 4,     /* M, N, K <= 0, K % block_size != 0, or a size
                               beyond the documented limits                    */
     MNB_ERR_DTYPE = 5,     /* dtype not MNB_F32 / MNB_F16, or not supported
@@ -105,6 +105,12 @@ size_t mnb_packed_bytes(int64_t N, int64_t K, int bits, int block_size, int dtyp
  * and zp = q = 0 for a block whose stored scale is 0. rint rounds half to
  * even. w: device float32 [N][K]. Outputs: qweight [N][K/2], scales
  * [N][K/bs] of dtype, zero_points [N][ceil(K/bs/2)] (canonical layout).
+ *
+ * zero_points NULL selects the symmetric format (the is_symmetric setting of
+ * the same conversion, "Mega-ASR INT4 ONNX", section "Conversion details"):
+ * no zero points are stored, every block uses the fixed zero point 8 (the
+ * middle of the 4-bit range), and s = max|w| / 7 rounded once to dtype, so
+ * that q = clamp(rint(w / s) + 8, 0, 15) never clips; q = 8 where s is 0.
  * Weights must be finite. Not a hot-path call (offline tooling).
  */
 int mnb_quantize_rtn(const float *w, int64_t N, int64_t K, int bits, int block_size, int dtype,
@@ -113,6 +119,8 @@ int mnb_quantize_rtn(const float *w, int64_t N, int64_t K, int bits, int block_s
 /*
  * Canonical format -> the device layout the compute kernels read, written to
  * `packed` (mnb_packed_bytes(...) bytes, device). Runs once per weight.
+ * zero_points NULL: the symmetric format, stored as zero point 8 for every
+ * block (the compute kernels then run unchanged).
  */
 int mnb_pack(const uint8_t *qweight, const void *scales, const uint8_t *zero_points,
              int64_t N, int64_t K, int bits, int block_size, int dtype,

@@ -24,6 +24,9 @@ notes. The functions and what pins each one (tests/test_oracle_pins.py):
   rtn_quantize        pinned: nearest-grid-point brute force, on-grid blocks,
                       RNE tie block, single-signed and all-zero blocks,
                       round-trip error bound
+  rtn_quantize_symmetric
+                      pinned: on-grid blocks, RNE tie, all-zero block,
+                      nearest-grid-point brute force, no clipping
   pack_nibbles /
   unpack_nibbles      pinned: all 256 byte values against divmod, round trip
   dequantize_exact    pinned: Fraction arithmetic, integrality of D/s
@@ -39,6 +42,8 @@ notes. The functions and what pins each one (tests/test_oracle_pins.py):
 from .mnb_oracle import (  # noqa: F401
     QMAX,
     rtn_quantize,
+    rtn_quantize_symmetric,
+    SYM_ZP,
     pack_nibbles,
     unpack_nibbles,
     pack_weight,

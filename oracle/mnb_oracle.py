@@ -6,8 +6,8 @@ blocking, fusion or reordering beyond what each definition states.
 
 Notation, following the model-card pages ("Mega-ASR INT4 ONNX", section
 "Conversion details"; "Qwen3-ASR-0.6B ONNX for the browser", section "Pick a
-variant"): a weight W has N output rows and K inputs; blocks of `bs` (32 or
-64) consecutive inputs of one row share one scale `s` and one 4-bit zero
+variant"): a weight W has N output rows and K inputs; blocks of `bs` (32, 64
+or 128) consecutive inputs of one row share one scale `s` and one 4-bit zero
 point `zp`; codes `q` are 4-bit unsigned. MatMulNBits computes
 Y[M, N] = X[M, K] @ D[N, K]^T with D = (q - zp) * s.
 
@@ -80,6 +80,43 @@ def rtn_quantize(w, block_size, scale_dtype):
     return (q.reshape(n_rows, k).astype(np.uint8),
             scale,
             zp.astype(np.uint8))
+
+
+SYM_ZP = 1 << (BITS - 1)  # 8: the zero point of the symmetric format
+SYM_QMAX = SYM_ZP - 1      # 7: largest magnitude the symmetric scale maps to
+
+
+def rtn_quantize_symmetric(w, block_size, scale_dtype):
+    """Round-to-nearest symmetric 4-bit quantization of W[N, K] (the
+    is_symmetric setting of the conversion, "Mega-ASR INT4 ONNX", section
+    "Conversion details"; the pages use it off, and define nothing more, so
+    this follows the usual symmetric form). Per block:
+
+      1. a = max |w|
+      2. s = round_to_scale_dtype(a / 7)                     (float64 divide)
+      3. q = clamp(rint(w / s) + 8, 0, 15)    (the zero point is fixed at 8)
+    A block whose stored scale is zero gets q = 8.
+
+    Returns (q uint8 [N, K], scales [N, K/bs], zero_points uint8 [N, K/bs]
+    all equal to 8), so that dequantize() and matmul_nbits() apply as they are.
+    """
+    w = np.asarray(w)
+    if w.ndim != 2:
+        raise ValueError("W must be 2-D [N, K]")
+    n_rows, k = w.shape
+    nb = _blocks(k, block_size)
+    blocks = w.astype(np.float64).reshape(n_rows, nb, block_size)
+
+    amax = np.abs(blocks).max(axis=2)
+    scale = (amax / SYM_QMAX).astype(scale_dtype)  # one rounding to the stored dtype
+    s = scale.astype(np.float64)
+
+    live = s != 0.0
+    s_div = np.where(live, s, 1.0)
+    q = np.clip(np.rint(blocks / s_div[:, :, None]) + SYM_ZP, 0, QMAX)
+    q = np.where(live[:, :, None], q, float(SYM_ZP))
+    zp = np.full((n_rows, nb), SYM_ZP, dtype=np.uint8)
+    return q.reshape(n_rows, k).astype(np.uint8), scale, zp
 
 
 # ---------------------------------------------------------------------------

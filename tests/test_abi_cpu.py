@@ -53,7 +53,8 @@ def _expected_bytes(n, k, bs, sb):
 
 
 @pytest.mark.parametrize("n,k,bs,dt", [(3072, 1024, 32, 0), (151936, 1024, 32, 1), (768, 3072, 64, 1),
-                                       (17, 96, 32, 1), (1, 32, 32, 0), (5, 64, 64, 1)])
+                                       (17, 96, 32, 1), (1, 32, 32, 0), (5, 64, 64, 1), (2048, 1024, 128, 1),
+                                       (33, 384, 128, 0)])
 def test_packed_bytes(L, n, k, bs, dt):
     assert L.mnb_packed_bytes(n, k, 4, bs, dt) == _expected_bytes(n, k, bs, 4 if dt == 0 else 2)
 
@@ -80,7 +81,7 @@ ODD = ctypes.c_void_p((1 << 20) + 8)
 @pytest.mark.parametrize("call,status", [
     (lambda L: L.mnb_gemv(None, FAKE2, FAKE3, 64, 64, 4, 32, 1, None), NULL),
     (lambda L: L.mnb_gemv(FAKE, FAKE2, FAKE3, 64, 64, 8, 32, 1, None), BITS),
-    (lambda L: L.mnb_gemv(FAKE, FAKE2, FAKE3, 64, 64, 4, 128, 1, None), BLOCK),
+    (lambda L: L.mnb_gemv(FAKE, FAKE2, FAKE3, 64, 64, 4, 96, 1, None), BLOCK),
     (lambda L: L.mnb_gemv(FAKE, FAKE2, FAKE3, 64, 64, 4, 32, 7, None), DTYPE),
     (lambda L: L.mnb_gemv(FAKE, FAKE2, FAKE3, 64, 48, 4, 32, 1, None), SHAPE),
     (lambda L: L.mnb_gemv(FAKE, FAKE2, FAKE3, -1, 64, 4, 32, 1, None), SHAPE),
@@ -88,7 +89,11 @@ ODD = ctypes.c_void_p((1 << 20) + 8)
     (lambda L: L.mnb_gemm(FAKE, FAKE2, FAKE3, 0, 64, 64, 4, 32, 1, None), SHAPE),
     (lambda L: L.mnb_gemm(FAKE, FAKE2, ODD, 8, 64, 64, 4, 32, 1, None), ALIGN),
     (lambda L: L.mnb_gemm(FAKE, FAKE2, FAKE3, 8, 64, 40000, 4, 32, 1, None), SHAPE),
-    (lambda L: L.mnb_pack(FAKE, FAKE2, None, 64, 64, 4, 32, 1, FAKE3, None), NULL),
+    (lambda L: L.mnb_pack(None, FAKE2, None, 64, 64, 4, 32, 1, FAKE3, None), NULL),
+    (lambda L: L.mnb_pack(FAKE, FAKE2, None, 64, 64, 4, 256, 1, FAKE3, None), BLOCK),
+    (lambda L: L.mnb_pack(FAKE, FAKE2, None, 64, 64, 4, 16, 1, FAKE3, None), BLOCK),
+    (lambda L: L.mnb_quantize_rtn(FAKE, 64, 64, 4, 32, 1, FAKE2, None, None, None), NULL),
+    (lambda L: L.mnb_gemv(FAKE, FAKE2, FAKE3, 64, 192, 4, 128, 1, None), SHAPE),
     (lambda L: L.mnb_pack(FAKE, FAKE2, FAKE3, 64, 64, 4, 64, 1, ODD, None), ALIGN),
     (lambda L: L.mnb_unpack(FAKE, 64, 64, 4, 32, 1, None, FAKE3, None), NULL),
     (lambda L: L.mnb_dequant(FAKE, 64, 65, 4, 32, 1, FAKE2, None), SHAPE),

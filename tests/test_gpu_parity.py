@@ -180,7 +180,7 @@ def test_errors_raise_and_enqueue_nothing():
 # (one grouped plan over the config's linears), checked on sampled rows.
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("ci", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("ci", [0, 1, 2, 3, 4, 5, 6, 7])
 def test_full_size_config_sampled(ci):
     from block_wise_int4_amd import workload
     cfg = configs.CONFIGS[ci]
@@ -193,10 +193,11 @@ def test_full_size_config_sampled(ci):
     dt = np.float16 if cfg.dtype == "f16" else np.float32
     for ld in data.linears:
         rows = ld.sample_rows
-        q, s, zp = oracle.rtn_quantize(ld.w_rows, cfg.block_size, dt)
+        quantize = oracle.rtn_quantize_symmetric if cfg.symmetric else oracle.rtn_quantize
+        q, s, zp = quantize(ld.w_rows, cfg.block_size, dt)
         gq, gs, gz = ld.canonical
         qw, pz = oracle.pack_weight(q, zp)
-        assert np.array_equal(gq, qw) and np.array_equal(gz, pz)
+        assert np.array_equal(gq, qw) and (gz is None if cfg.symmetric else np.array_equal(gz, pz))
         assert np.array_equal(gs.view(np.uint8), s.view(np.uint8))
         x = ld.x.cpu().numpy()
         mrows = np.unique(np.linspace(0, cfg.m - 1, min(cfg.m, 6)).astype(int))

@@ -426,3 +426,68 @@ def test_embedding_dequant_exact(dtype):
     for r, i in enumerate(ids):
         for c in range(16):
             assert frac(out[r, c]) == rne(int(table[i, c]) * frac(scales[i]), dtype)
+
+
+# ---------------------------------------------------------------------------
+# Symmetric format (fixed zero point 8, s = max|w| / 7)
+# ---------------------------------------------------------------------------
+
+def test_symmetric_on_grid_blocks_quantize_exactly():
+    bs = 32
+    rng = np.random.default_rng(15)
+    rows, want_q, want_e = [], [], []
+    for i in range(12):
+        e = 2 + i % 9
+        c = rng.integers(1, 16, size=bs)
+        c[rng.integers(0, bs)] = 1 if i % 2 else 15   # |c - 8| = 7 is present
+        rows.append((c.astype(np.float64) - 8) * 2.0 ** -e)
+        want_q.append(c)
+        want_e.append(e)
+    w = np.array(rows, dtype=np.float32)
+    for dtype in (np.float16, np.float32):
+        q, s, zp = oracle.rtn_quantize_symmetric(w, bs, dtype)
+        assert np.array_equal(q, np.array(want_q, dtype=np.uint8))
+        assert (zp == 8).all()
+        assert np.array_equal(s[:, 0].astype(np.float64), 2.0 ** -np.array(want_e, dtype=np.float64))
+        assert np.array_equal(oracle.dequantize_exact(q, zp, s, bs), w.astype(np.float64))
+
+
+def test_symmetric_tie_rounds_half_to_even_and_zero_block():
+    sc = 2.0 ** -7
+    blk = np.zeros(32)
+    blk[:5] = np.array([7.0, 2.5, -1.5, 0.5, -7.0]) * sc
+    w = np.stack([blk, np.zeros(32)]).astype(np.float32)
+    q, s, zp = oracle.rtn_quantize_symmetric(w, 32, np.float16)
+    assert float(s[0, 0]) == sc
+    assert list(q[0, :5]) == [15, 10, 6, 8, 1]   # 7, rint(2.5) = 2, rint(-1.5) = -2, rint(0.5) = 0, -7
+    assert float(s[1, 0]) == 0.0 and (q[1] == 8).all()
+
+
+@pytest.mark.parametrize("dtype,bs", [(np.float16, 32), (np.float32, 64), (np.float16, 128)])
+def test_symmetric_codes_are_nearest_grid_points(dtype, bs):
+    rng = np.random.default_rng(bs)
+    w = (rng.standard_normal((6, 2 * bs)) * 0.02).astype(np.float32)
+    q, s, zp = oracle.rtn_quantize_symmetric(w, bs, dtype)
+    assert q.min() >= 1   # max|w| / s <= 7: the code 0 (offset -8) is never needed
+    for i in range(w.shape[0]):
+        for b in range(w.shape[1] // bs):
+            sb = frac(s[i, b])
+            for j in range(bs):
+                v = frac(w[i, b * bs + j])
+                dist = [abs(v - (c - 8) * sb) for c in range(16)]
+                best = min(dist)
+                cands = [c for c in range(16) if dist[c] == best]
+                c = int(q[i, b * bs + j])
+                assert c in cands
+                if len(cands) == 2:
+                    assert (c - 8) % 2 == 0
+
+
+@pytest.mark.parametrize("dtype,u", [(np.float16, 2.0 ** -11), (np.float32, 2.0 ** -24)])
+def test_symmetric_round_trip_bound(dtype, u):
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((40, 256)) * 0.02).astype(np.float32)
+    q, s, zp = oracle.rtn_quantize_symmetric(w, 64, dtype)
+    d = oracle.dequantize_exact(q, zp, s, 64)
+    err = np.abs(w.astype(np.float64) - d).reshape(40, 4, 64).max(axis=2)
+    assert (err <= s.astype(np.float64) * (0.5 + 7 * u)).all()

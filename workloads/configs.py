@@ -20,6 +20,9 @@ Linear shapes are (N outputs, K inputs), i.e. W is [N, K] and Y = X @ W^T.
   formula, plus about 20 prompt rows; the decoder that takes such chunks
   after a cached prefix is the merged one, quantized at block 64
   ("qwen3-asr-0.6b-onnx-int4-merged", sections "Why" and "Provenance").
+* Format variants: the same decode step at block 128, and with symmetric
+  codes (the is_symmetric setting, "Mega-ASR INT4 ONNX", section
+  "Conversion details", which those exports leave off).
 """
 
 from dataclasses import dataclass, field
@@ -65,6 +68,7 @@ class Config:
     block_size: int
     dtype: str              # activation dtype == scale dtype: "f32" or "f16"
     linears: tuple = field(default_factory=tuple)
+    symmetric: bool = False  # no zero points (fixed zero point 8)
 
     @property
     def kind(self):
@@ -85,6 +89,9 @@ CONFIGS = (
     Config(3, "qwen3-1.7b-prefill-m410", 410, 32, "f16", _stack(QWEN3_17B_LAYER, 28)),
     Config(4, "whisper-small-encoder-m1500-bs64", 1500, 64, "f16", _stack(WHISPER_SMALL_LAYER, 12)),
     Config(5, "qwen3-0.6b-chunk-m62-bs64", 62, 64, "f16", _stack(QWEN3_06B_LAYER, 28)),
+    # format variants of the 0.6B decode step: block 128, and symmetric codes
+    Config(6, "qwen3-0.6b-decode-step-bs128", 1, 128, "f16", _stack(QWEN3_06B_LAYER, 28, 1024)),
+    Config(7, "qwen3-0.6b-decode-step-symmetric", 1, 32, "f16", _stack(QWEN3_06B_LAYER, 28, 1024), True),
 )
 
 PROJ_INDEX = {p: i for i, p in enumerate(
