@@ -23,6 +23,13 @@
 // either side. Two operand slots alternate: slice t is multiplied from one
 // while slice t + 1 is dequantized into the other.
 //
+// Instruction order. A stage runs as one fixed sequence (pinned with
+// scheduling barriers): each step issues a fragment's MFMAs, the LDS read of
+// the fragment MNB_GEMM_PIPE steps later into a small register ring, and one
+// float16 pair of the next slice's weights. The compiler's own order, under
+// this kernel's register pressure, left each read one step ahead and
+// waited for every read.
+//
 // Activation side: the 128-input tile is split in two LDS stages of 64
 // inputs (stage h feeds slices t = 2h, 2h+1). A stage is a list of 1 KB
 // lines, one per (16-row fragment, slice): byte 16*l of a line holds the 8
@@ -46,8 +53,8 @@ namespace mnb {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-#ifndef MNB_GEMM_SCHED
-#define MNB_GEMM_SCHED 5  // A-fragment reads kept ahead of the MFMAs (0: compiler's order)
+#ifndef MNB_GEMM_PIPE
+#define MNB_GEMM_PIPE 5  // A-fragment reads kept in flight ahead of the MFMAs that use them
 #endif
 
 template <int MF, int NF, int WM, int WN>
@@ -237,36 +244,6 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
 #pragma unroll
         for (int b = 0; b < NF; ++b) acc[a][b] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // one slice: each A fragment of the wave (line 2a + tt of the stage)
-    // times the slice's B operands
-    auto phase = [&](int64_t stage, int tt, const h8 (&bw)[NF]) {
-        const uint8_t *As = lds + (int)((uint32_t)stage % (uint32_t)C::kBufs) * C::kStageBytes +
-                            (wm * MF * 2 + tt) * 1024 + lane * 16;
-#pragma unroll
-        for (int a = 0; a < MF; ++a) {
-            const h8 av = *reinterpret_cast<const h8 *>(As + a * 2048);
-#pragma unroll
-            for (int b = 0; b < NF; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bw[b], acc[a][b], 0, 0, 0);
-        }
-    };
-    // Instruction order of a slice: the fragment reads run MNB_GEMM_SCHED
-    // ahead of the MFMAs that use them, and the next slice's dequant
-    // arithmetic is spread between the MFMA groups.
-    auto schedule_phase = [&]() {
-#if MNB_GEMM_SCHED
-        constexpr int kAhead = MNB_GEMM_SCHED < MF ? MNB_GEMM_SCHED : MF;
-        constexpr int kValu = (NF * 16 + MF - 1) / MF;
-        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
-#pragma unroll
-        for (int i = 0; i < MF; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, NF, 0);
-            if (i + kAhead < MF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
-        }
-#endif
-    };
-
     const int64_t n_stages = 2 * p.kg;
     // a wave may own one line fewer than kLinesPerWave; it waits for its own count
     const bool full_lines = wave + (C::kLinesPerWave - 1) * C::kWaves < C::kLines;
@@ -293,30 +270,73 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     // first, so that at each stage end only the newest lines may be pending.
     h8 s0[NF], s1[NF];
     const int64_t n_groups = (p.kg + kMetaGroup - 1) / kMetaGroup;
+    // One stage, both slices, in a fixed order: the A fragments of the stage
+    // (slice 0's 13 lines, then slice 1's) stream through a ring of
+    // MNB_GEMM_PIPE registers, each read issued that many MFMA groups before
+    // its use; each step also forms one float16 pair of the next slice's B
+    // operands (slice 0 fills s1 from Ra, slice 1 fills s0 from Rb).
+    auto put_pair = [&](const BRaw<NF> &R, int t, int b, int hh, h8 &dst) {
+        const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)R.s[b]);
+        const h2 zm = zp_magic(R.z[b] & 15u);
+        const h2 s2 = {s, s};
+        const u32x4 w = R.codes[b];
+        const h2 d = dequant_pair_f16(w[t], hh, zm, s2);
+        dst[2 * hh] = d.x;
+        dst[2 * hh + 1] = d.y;
+    };
+    auto run_stage = [&](int64_t stage, const BRaw<NF> &Ra, int ta, const BRaw<NF> &Rb, int tb) {
+        constexpr int R = MNB_GEMM_PIPE < 2 * MF ? MNB_GEMM_PIPE : 2 * MF;
+        constexpr int kPieces = NF * 4;
+        const uint8_t *base = lds + (int)((uint32_t)stage % (uint32_t)C::kBufs) * C::kStageBytes +
+                              (wm * MF * 2) * 1024 + lane * 16;
+        h8 ring[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) ring[i] = *reinterpret_cast<const h8 *>(base + ((i % MF) * 2 + i / MF) * 1024);
+#pragma unroll
+        for (int q = 0; q < 2 * MF; ++q) {
+            const int tt = q / MF, a = q % MF;
+            const h8 av = ring[q % R];
+#pragma unroll
+            for (int b = 0; b < NF; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, tt == 0 ? s0[b] : s1[b], acc[a][b], 0, 0, 0);
+            if (q + R < 2 * MF) {
+                const int qq = q + R;
+                ring[q % R] = *reinterpret_cast<const h8 *>(base + ((qq % MF) * 2 + qq / MF) * 1024);
+            }
+            if (a < kPieces) {
+                if (tt == 0) put_pair(Ra, ta, a / 4, a % 4, s1[a / 4]);
+                else put_pair(Rb, tb, a / 4, a % 4, s0[a / 4]);
+            }
+            if (a == MF - 1) {  // pieces the slice had no step left for
+#pragma unroll
+                for (int k = MF; k < kPieces; ++k) {
+                    if (tt == 0) put_pair(Ra, ta, k / 4, k % 4, s1[k / 4]);
+                    else put_pair(Rb, tb, k / 4, k % 4, s0[k / 4]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
     auto tile = [&](int64_t c, const BRaw<NF> &Rc, BRaw<NF> &Rn) {
         const bool more = c + 1 < p.kg;
-        // the next tile group's metadata, into the slot group c / 8 - 1 used
         if (c % kMetaGroup == 0 && c / kMetaGroup + 1 < n_groups) issue_meta(c / kMetaGroup + 1);
         if (more) load_b(c + 1, Rn);
         issue_ahead(2 * c);
-        phase(2 * c, 0, s0);
-        dequant_t(Rc, 1, s1);
-        schedule_phase();
-        phase(2 * c, 1, s1);
-        dequant_t(Rc, 2, s0);
-        schedule_phase();
+        run_stage(2 * c, Rc, 1, Rc, 2);
         stage_sync(2 * c);
         issue_ahead(2 * c + 1);
-        phase(2 * c + 1, 0, s0);
-        dequant_t(Rc, 3, s1);
-        schedule_phase();
-        phase(2 * c + 1, 1, s1);
-        if (more) dequant_t(Rn, 0, s0);
-        schedule_phase();
+        // (after the last K-tile Rn holds no weights; its slice is formed and never used)
+        run_stage(2 * c + 1, Rc, 3, Rn, 0);
         stage_sync(2 * c + 1);
     };
 
     BRaw<NF> R0, R1;
+#pragma unroll
+    for (int b = 0; b < NF; ++b) {
+        R1.codes[b] = u32x4{0u, 0u, 0u, 0u};
+        R1.s[b] = 0u;
+        R1.z[b] = 0u;
+    }
     // metadata, codes and lines of the first K-tile all in flight at once
     issue_meta(0);
     load_codes(0, R0);
