@@ -283,12 +283,22 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     // multiplies from slot t & 1).
     h8 s0[NF], s1[NF];
     const int64_t n_groups = (p.kg + kMetaGroup - 1) / kMetaGroup;
+    // The nibble mask and the 1024 offset held in registers (literal
+    // constants cannot go into the three-operand form), so that masking a
+    // pair and adding the offset is one v_and_or_b32.
+    uint32_t pair_mask = 0x000F000Fu, pair_magic = 0x64006400u;
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(pair_mask));
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(pair_magic));
+#endif
+    // the same exact (q - zp) pair times the scale as dequant_pair_f16
     auto put_pair = [&](const BRaw<NF> &R, int t, int b, int hh, h8 &dst) {
         const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)R.s[b]);
         const h2 zm = zp_magic(R.z[b] & 15u);
         const h2 s2 = {s, s};
         const u32x4 w = R.codes[b];
-        const h2 d = dequant_pair_f16(w[t], hh, zm, s2);
+        const uint32_t word = hh ? w[t] >> (4 * hh) : w[t];
+        const h2 d = (as_h2((word & pair_mask) | pair_magic) - zm) * s2;
         dst[2 * hh] = d.x;
         dst[2 * hh + 1] = d.y;
     };
