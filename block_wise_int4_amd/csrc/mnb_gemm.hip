@@ -6,7 +6,11 @@
 // block of Y, so the workgroup tile is (WM * MF * 16) x (WN * NF * 16). The
 // large-M tiles are 208 (or 192) rows by 256 columns, 8 waves of 208 x 32:
 // the accumulators (104 registers) leave room for two waves per SIMD, so one
-// wave's MFMAs overlap the other's loads and dequantization.
+// wave's MFMAs overlap the other's loads and dequantization. Up to 64 rows
+// the tiles are 16, 32 or 64 rows by 256 columns, 4 waves of 64 columns
+// each: every wave reads all of the workgroup's activation rows from LDS,
+// so wide waves halve that traffic per weight and halve the number of
+// workgroups (each of which pays a prologue of roughly one memory latency).
 //
 // Weight side: a wave owns NF 16-row groups of W (= NF 16-column fragments
 // of Y). For each 128-input tile it issues one coalesced 128-bit load per
@@ -62,7 +66,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 #define MNB_GEMM_STAGE_SLICES 4  // k-slices per LDS stage: 4 (a whole 128-input tile) or 2 (64 inputs)
 #endif
 
-template <int MF, int NF, int WM, int WN>
+template <int MF, int NF, int WM, int WN, int MaxBufs>
 struct GemmCfg {
     static constexpr int kMT = WM * MF * 16;
     static constexpr int kNT = WN * NF * 16;
@@ -77,8 +81,9 @@ struct GemmCfg {
     // scales (up to 64 entries x 8 tiles = 1 KB) and zero points (256 B)
     static constexpr int kMetaScaleBytes = 1024, kMetaZpBytes = 256;
     static constexpr int kMetaBytes = kWaves * 2 * NF * (kMetaScaleBytes + kMetaZpBytes);
-    // as many stage buffers as fit in the CU's 160 KB next to the metadata (at most 3)
-    static constexpr int kBufs = 3 * kStageBytes + kMetaBytes <= 160 * 1024 ? 3 : 2;
+    // as many stage buffers as fit in the CU's 160 KB next to the metadata
+    // (at most MaxBufs: 2 or 3)
+    static constexpr int kBufs = MaxBufs >= 3 && 3 * kStageBytes + kMetaBytes <= 160 * 1024 ? 3 : 2;
     static_assert(kSlices == 2 || kSlices == 4, "a stage holds 2 or 4 k-slices");
     static constexpr int kMetaOff = kBufs * kStageBytes;
     // epilogue staging: each wave's (MF * 16) x (NF * 16) float16 block
@@ -128,9 +133,9 @@ struct BRaw {
     uint32_t z[NF];  // its zero point (low nibble)
 };
 
-template <int MF, int NF, int WM, int WN>
+template <int MF, int NF, int WM, int WN, int MaxBufs>
 __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uint8_t *lds) {
-    using C = GemmCfg<MF, NF, WM, WN>;
+    using C = GemmCfg<MF, NF, WM, WN, MaxBufs>;
     const int64_t tn = wg % p.tiles_n;
     const int64_t tm = wg / p.tiles_n;
     const int64_t m0 = tm * C::kMT;
@@ -360,17 +365,23 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
         R1.s[b] = 0u;
         R1.z[b] = 0u;
     }
-    // metadata, codes and lines of the first K-tile all in flight at once
+    // metadata, codes and lines of the first K-tile all in flight at once;
+    // the metadata is issued first (pinned by a scheduling barrier), since
+    // the wait below counts the loads issued after it
+    const bool two = C::kBufs == 3 && n_stages > 1;
     issue_meta(0);
+    __builtin_amdgcn_sched_barrier(0);
     load_codes(0, R0);
     issue_a(0);
-    if (C::kBufs == 3 && n_stages > 1) issue_a(1);
+    if (two) issue_a(1);
     // tile group 0's metadata has landed once at most one code load and the
-    // lines are pending (a wave with metadata issued a code load after it)
-    wait_vmem<1 + (C::kBufs == 3 ? 2 : 1) * (C::kLinesPerWave - 1)>();
+    // lines are pending (a wave with metadata issued a code load after it,
+    // and at least kLinesPerWave - 1 lines per stage)
+    if (two) wait_vmem<1 + 2 * (C::kLinesPerWave - 1)>();
+    else wait_vmem<1 + C::kLinesPerWave - 1>();
     read_meta(0, R0);
     dequant_t(R0, 0, s0);
-    if (C::kBufs == 3 && n_stages > 1) {
+    if (two) {
         if (full_lines) wait_vmem<C::kLinesPerWave>();
         else wait_vmem<C::kLinesPerWave - 1>();
     } else {
@@ -432,10 +443,10 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     }
 }
 
-template <int MF, int NF, int WM, int WN>
+template <int MF, int NF, int WM, int WN, int MaxBufs>
 __global__ __launch_bounds__(64 * WM *WN) void gemm_kernel(Problem p) {
-    __shared__ __align__(1024) uint8_t lds[GemmCfg<MF, NF, WM, WN>::kLdsBytes];
-    gemm_workgroup<MF, NF, WM, WN>(p, xcd_logical_wg(blockIdx.x, gridDim.x), lds);
+    __shared__ __align__(1024) uint8_t lds[GemmCfg<MF, NF, WM, WN, MaxBufs>::kLdsBytes];
+    gemm_workgroup<MF, NF, WM, WN, MaxBufs>(p, xcd_logical_wg(blockIdx.x, gridDim.x), lds);
 }
 
 __device__ __forceinline__ int find_gemm_problem(const Problem *entries, int count, int64_t wg) {
@@ -451,30 +462,47 @@ __device__ __forceinline__ int find_gemm_problem(const Problem *entries, int cou
 // Grouped launches: XCD x (blocks b with b % 8 == x) runs its own tile range
 // (whole products, balanced by work on the host, longest K first); blocks
 // past the end of their XCD's range exit at once.
-template <int MF, int NF, int WM, int WN>
+template <int MF, int NF, int WM, int WN, int MaxBufs>
 __global__ __launch_bounds__(64 * WM *WN) void gemm_grouped_kernel(const Problem *entries, int count,
                                                                    XcdSplit split) {
-    __shared__ __align__(1024) uint8_t lds[GemmCfg<MF, NF, WM, WN>::kLdsBytes];
+    __shared__ __align__(1024) uint8_t lds[GemmCfg<MF, NF, WM, WN, MaxBufs>::kLdsBytes];
     const int x = (int)(blockIdx.x % kXcds);
     const int64_t wg = split.begin[x] + (int64_t)(blockIdx.x / kXcds);
     if (wg >= split.begin[x + 1]) return;
     const int i = find_gemm_problem(entries, count, wg);
     const Problem p = entries[i];
-    gemm_workgroup<MF, NF, WM, WN>(p, wg - p.wg_begin, lds);
+    gemm_workgroup<MF, NF, WM, WN, MaxBufs>(p, wg - p.wg_begin, lds);
 }
 
 // ---------------------------------------------------------------------------
 // Variants and their selection.
 // ---------------------------------------------------------------------------
+// 16-row fragments (NF) per wave of the small-M tiles
+#ifndef MNB_GEMM_NF0
+#define MNB_GEMM_NF0 4
+#endif
+#ifndef MNB_GEMM_NF1
+#define MNB_GEMM_NF1 4
+#endif
+#ifndef MNB_GEMM_NF2
+#define MNB_GEMM_NF2 4
+#endif
+// stage buffers at most, per tile shape
+#ifndef MNB_GEMM_BUFS_SMALL
+#define MNB_GEMM_BUFS_SMALL 3
+#endif
+#ifndef MNB_GEMM_BUFS_MID
+#define MNB_GEMM_BUFS_MID 2
+#endif
 struct VariantInfo {
     int mt, nt;
 };
 static const VariantInfo kVariants[] = {
-    {16, 64},    // 0: MF 1,  NF 1, 1x4 waves
-    {32, 64},    // 1: MF 2,  NF 1, 1x4 waves
-    {64, 128},   // 2: MF 4,  NF 2, 1x4 waves
-    {208, 256},  // 3: MF 13, NF 2, 1x8 waves
-    {192, 256},  // 4: MF 12, NF 2, 1x8 waves
+    {16, 64 * MNB_GEMM_NF0},  // 0: MF 1,  1x4 waves
+    {32, 64 * MNB_GEMM_NF1},  // 1: MF 2,  1x4 waves
+    {64, 64 * MNB_GEMM_NF2},  // 2: MF 4,  1x4 waves
+    {208, 256},               // 3: MF 13, NF 2, 1x8 waves
+    {192, 256},               // 4: MF 12, NF 2, 1x8 waves
 };
 constexpr int kNumVariants = 5;
 
@@ -506,18 +534,19 @@ void gemm_tiles(const Problem &p, int variant, int32_t *tiles_m, int32_t *tiles_
     *tiles_n = (int32_t)((p.rg + rg_per_tile - 1) / rg_per_tile);
 }
 
-#define MNB_GEMM_VARIANTS(X) \
-    X(0, 1, 1, 1, 4)         \
-    X(1, 2, 1, 1, 4)         \
-    X(2, 4, 2, 1, 4)         \
-    X(3, 13, 2, 1, 8)        \
-    X(4, 12, 2, 1, 8)
+// (variant, MF, NF, WM, WN, stage buffers at most)
+#define MNB_GEMM_VARIANTS(X)                          \
+    X(0, 1, MNB_GEMM_NF0, 1, 4, MNB_GEMM_BUFS_SMALL)  \
+    X(1, 2, MNB_GEMM_NF1, 1, 4, MNB_GEMM_BUFS_SMALL)  \
+    X(2, 4, MNB_GEMM_NF2, 1, 4, MNB_GEMM_BUFS_MID)    \
+    X(3, 13, 2, 1, 8, 3)                              \
+    X(4, 12, 2, 1, 8, 3)
 
 hipError_t launch_gemm(const Problem &p, int variant, hipStream_t st) {
     const unsigned grid = (unsigned)((int64_t)p.tiles_m * p.tiles_n);
     switch (variant) {
-#define X(V, MF, NF, WM, WN) \
-    case V: gemm_kernel<MF, NF, WM, WN><<<grid, 64 * WM * WN, 0, st>>>(p); break;
+#define X(V, MF, NF, WM, WN, B) \
+    case V: gemm_kernel<MF, NF, WM, WN, B><<<grid, 64 * WM * WN, 0, st>>>(p); break;
         MNB_GEMM_VARIANTS(X)
 #undef X
     default: return hipErrorInvalidValue;
@@ -572,8 +601,9 @@ hipError_t launch_gemm_grouped(const Problem *dev_entries, int count, const XcdS
         if (split.begin[x + 1] - split.begin[x] > widest) widest = split.begin[x + 1] - split.begin[x];
     const int64_t wgs = widest * kXcds;
     switch (variant) {
-#define X(V, MF, NF, WM, WN) \
-    case V: gemm_grouped_kernel<MF, NF, WM, WN><<<(unsigned)wgs, 64 * WM * WN, 0, st>>>(dev_entries, count, split); \
+#define X(V, MF, NF, WM, WN, B)                                                                            \
+    case V:                                                                                                \
+        gemm_grouped_kernel<MF, NF, WM, WN, B><<<(unsigned)wgs, 64 * WM * WN, 0, st>>>(dev_entries, count, split); \
         break;
         MNB_GEMM_VARIANTS(X)
 #undef X

@@ -110,7 +110,11 @@ def test_gemv_parity(n, k, bs, dt):
 GEMM_CASES = [(2, 64, 64, 32), (7, 200, 256, 32), (16, 1024, 2048, 32), (17, 96, 96, 32), (31, 130, 512, 64),
               (33, 64, 1024, 32), (64, 300, 4160, 32), (65, 512, 768, 64), (100, 256, 2048, 32),
               (130, 1024, 768, 64), (257, 384, 1024, 32), (410, 1024, 2048, 32), (500, 200, 3072, 64),
-              (1500, 768, 768, 64)]
+              (1500, 768, 768, 64),
+              # one K-tile (with and without a ragged tail) and K-loops shorter or a little longer than
+              # each tile shape's ring of prefetched code tiles
+              (40, 64, 128, 32), (48, 200, 96, 32), (70, 100, 128, 32), (60, 130, 384, 64), (64, 256, 640, 32),
+              (12, 100, 896, 32), (16, 64, 2176, 32), (30, 70, 1152, 64), (62, 3072, 1024, 64)]
 
 
 @pytest.mark.parametrize("m,n,k,bs", GEMM_CASES)
