@@ -118,8 +118,8 @@ def time_steps(fn_list, steps, warmup, torch, per_launch=False):
     """Run fn_list[i % R]() for warmup + steps and time the last `steps` with
     HIP events on the current stream (the stream the kernels run on).
     Returns (ms per step, list of per-call ms or None). With per_launch, an
-    event pair also brackets every timed call; for a one-launch step that is
-    the kernel's own duration."""
+    event pair also brackets every timed call (a diagnostic: each pair adds
+    several microseconds between the launches it separates)."""
     R = len(fn_list)
     for i in range(warmup):
         fn_list[i % R]()
@@ -141,7 +141,7 @@ def time_steps(fn_list, steps, warmup, torch, per_launch=False):
     return start.elapsed_time(end) / steps, per
 
 
-def run_workload(cfg, steps, warmup, per_linear, torch, dev):
+def run_workload(cfg, steps, warmup, per_linear, torch, dev, launch_events=False):
     from block_wise_int4_amd import mnb, workload
 
     t0 = time.time()
@@ -159,16 +159,20 @@ def run_workload(cfg, steps, warmup, per_linear, torch, dev):
         f"({replicas * (weight_bytes + io_bytes) / 1e9:.2f} GB resident)")
 
     launches = mnb.mnb_plan_launches(plans[0])
-    ms, per = time_steps([lambda p=p: mnb.mnb_gemm_grouped(p) for p in plans], steps, warmup, torch,
-                         per_launch=launches == 1)
+    fns = [lambda p=p: mnb.mnb_gemm_grouped(p) for p in plans]
+    ms, _ = time_steps(fns, steps, warmup, torch)
     out = {"ms": ms, "bytes": algo, "flops": flops, "replicas": replicas, "launches_per_step": launches}
-    if per:
+    if launches == 1:
+        # the step is one launch, back to back: the region's time per step is
+        # the kernel's average duration (launch to launch)
+        out["launch_ms"] = ms
+    log(f"[bench] {cfg.name}: grouped {ms * 1e3:.1f} us/step ({launches} launches per step)")
+    if launch_events:
+        _, per = time_steps(fns, steps, warmup, torch, per_launch=True)
         srt = sorted(per)
-        out["launch_ms"] = sum(per) / len(per)
-        log(f"[bench] {cfg.name}: grouped {ms * 1e3:.1f} us/step; kernel avg {out['launch_ms'] * 1e3:.1f} us "
+        out["launch_ms_events"] = sum(per) / len(per)
+        log(f"[bench] {cfg.name}: with an event pair around each launch: avg {out['launch_ms_events'] * 1e3:.1f} us "
             f"(min {srt[0] * 1e3:.1f}, median {srt[len(srt) // 2] * 1e3:.1f}, max {srt[-1] * 1e3:.1f})")
-    else:
-        log(f"[bench] {cfg.name}: grouped {ms * 1e3:.1f} us/step ({launches} launches per step)")
     if per_linear:
         def one_pass(s):
             def f():
@@ -204,21 +208,18 @@ def run_lm_head_argmax(cfg, steps, warmup, torch, dev):
     ws = mnb.argmax_workspace(dev)
     idx = torch.empty(1, dtype=torch.int64, device=dev)
     y = torch.empty(lin.n, dtype=ld.y.dtype, device=dev)
-    ms_f, per_f = time_steps([lambda p=p: mnb.mnb_gemv_argmax(x, p, ws, index=idx) for p in pws], steps, warmup,
-                             torch, per_launch=True)
-    ms_g, per_g = time_steps([lambda p=p: mnb.mnb_gemv(x, p, y) for p in pws], steps, warmup, torch,
-                             per_launch=True)
-    kf, kg = sum(per_f) / len(per_f), sum(per_g) / len(per_g)
+    kf, _ = time_steps([lambda p=p: mnb.mnb_gemv_argmax(x, p, ws, index=idx) for p in pws], steps, warmup, torch)
+    kg, _ = time_steps([lambda p=p: mnb.mnb_gemv(x, p, y) for p in pws], steps, warmup, torch)
     bf = wbytes + lin.k * a + 8
     bg = wbytes + lin.k * a + lin.n * a
     log(f"[bench] {cfg.name} LM head {lin.n}x{lin.k}: fused argmax {kf * 1e3:.1f} us, plain {kg * 1e3:.1f} us")
     del pws
     torch.cuda.empty_cache()
     return {"shape": [lin.n, lin.k], "replicas": reps,
-            "fused_argmax": {"kernel_us": round(kf * 1e3, 2), "step_us": round(ms_f * 1e3, 2),
+            "fused_argmax": {"us_per_call": round(kf * 1e3, 2), "launches_per_call": 2,
                              "algorithmic_bytes": bf, "GBps": round(bf / (kf * 1e-3) / 1e9, 1),
                              "frac_hbm": round(bf / (kf * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
-            "plain_gemv": {"kernel_us": round(kg * 1e3, 2), "step_us": round(ms_g * 1e3, 2),
+            "plain_gemv": {"us_per_call": round(kg * 1e3, 2), "launches_per_call": 1,
                            "algorithmic_bytes": bg, "GBps": round(bg / (kg * 1e-3) / 1e9, 1)}}
 
 
@@ -244,11 +245,10 @@ def run_embed_gather(cfg, steps, warmup, torch, dev, token_counts=(410, 65536)):
         out = torch.empty((tokens, hidden), dtype=torch.float16, device=dev)
         fns = [lambda t=t, i=i: mnb.mnb_embed_gather(t, sc, i, torch.float16, out=out)
                for i in id_sets for t in tables]
-        ms, per = time_steps(fns, steps, warmup, torch, per_launch=True)
-        k = sum(per) / len(per)
+        k, _ = time_steps(fns, steps, warmup, torch)
         nbytes = tokens * hidden + tokens * 4 + tokens * 8 + tokens * hidden * 2
         log(f"[bench] embedding gather {tokens} x {hidden} of {vocab}: {k * 1e3:.1f} us")
-        res[f"tokens_{tokens}"] = {"kernel_us": round(k * 1e3, 2), "algorithmic_bytes": nbytes,
+        res[f"tokens_{tokens}"] = {"us_per_call": round(k * 1e3, 2), "algorithmic_bytes": nbytes,
                                    "GBps": round(nbytes / (k * 1e-3) / 1e9, 1),
                                    "frac_hbm": round(nbytes / (k * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del id_sets, out
@@ -303,6 +303,8 @@ def main():
     ap.add_argument("--no-per-linear", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true", help="skip the LM-head argmax and embedding-gather lines")
+    ap.add_argument("--launch-events", action="store_true",
+                    help="also time each launch between its own event pair (diagnostic; logged, not reported)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per workload")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this size (counter calibration runs)")
@@ -342,10 +344,13 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         log(f"[bench] copy probe: {n} bytes read, {n} bytes written")
+        ms_copy, _ = time_steps([lambda: b.copy_(a)], 10, 2, torch)
+        copy_gbs = 2 * n / (ms_copy * 1e-3) / 1e9
+        log(f"[bench] device copy of {args.copy_probe_mib} MiB: {ms_copy * 1e3:.1f} us = {copy_gbs:.0f} GB/s read+write")
         del a, b
 
     cfg = configs.CONFIGS[args.config]
-    dec = run_workload(cfg, args.steps, args.warmup, not args.no_per_linear, torch, dev)
+    dec = run_workload(cfg, args.steps, args.warmup, not args.no_per_linear, torch, dev, args.launch_events)
     gbs = dec["bytes"] / (dec["ms"] * 1e-3) / 1e9
     # one launch per step: the kernel's algorithmic bytes per launch are the step's
     k_gbs = dec["bytes"] / (dec.get("launch_ms", dec["ms"]) * 1e-3) / 1e9
@@ -380,6 +385,7 @@ def main():
             "frac": round(k_gbs / HBM_PEAK_GBS, 4),
             "traffic": dec_traffic,
             "kernel": decode_kernel, "launch_us": round(dec.get("launch_ms", dec["ms"]) * 1e3, 2),
+            "launch_timing": "timed region / steps (one launch per step, back to back)",
             "algorithmic_bytes_per_launch": dec["bytes"],
         },
     }
@@ -391,7 +397,7 @@ def main():
     if args.prefill_config >= 0:
         pcfg = configs.CONFIGS[args.prefill_config]
         pre = run_workload(pcfg, max(5, args.steps // 10), max(2, args.warmup // 10), not args.no_per_linear,
-                           torch, dev)
+                           torch, dev, args.launch_events)
         tf = pre["flops"] / (pre["ms"] * 1e-3) / 1e12
         k_tf = pre["flops"] / (pre.get("launch_ms", pre["ms"]) * 1e-3) / 1e12
         result["prefill"] = {
@@ -405,6 +411,7 @@ def main():
                          "traffic": stored_traffic(f"gemm_grouped_kernel:{pcfg.name}"),
                          "kernel": "gemm_grouped_kernel",
                          "launch_us": round(pre.get("launch_ms", pre["ms"]) * 1e3, 2),
+                         "launch_timing": "timed region / steps (one launch per step, back to back)",
                          "algorithmic_flops_per_launch": pre["flops"]},
         }
 
