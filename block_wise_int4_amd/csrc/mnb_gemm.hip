@@ -449,14 +449,22 @@ __global__ __launch_bounds__(64 * WM *WN) void gemm_kernel(Problem p) {
     gemm_workgroup<MF, NF, WM, WN, MaxBufs>(p, xcd_logical_wg(blockIdx.x, gridDim.x), lds);
 }
 
-__device__ __forceinline__ int find_gemm_problem(const Problem *entries, int count, int64_t wg) {
-    int lo = 0, hi = count - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (entries[mid].wg_begin <= wg) lo = mid;
-        else hi = mid - 1;
+// The product of entries[first, last) (tiles in increasing wg_begin order)
+// that holds tile wg: each lane reads one product's first tile, so a range
+// of up to 64 products costs one round trip, and a ballot counts the
+// products that start at or before wg. Wave-uniform; all 64 lanes active.
+__device__ __forceinline__ int find_gemm_problem(const Problem *entries, int first, int last, int64_t wg) {
+    const int lane = (int)(threadIdx.x & 63);
+    int found = first;
+    for (int base = first; base < last; base += 64) {
+        const int q = base + lane;
+        const int64_t wb = q < last ? entries[q].wg_begin : INT64_MAX;
+        const int k = __builtin_popcountll(__builtin_amdgcn_ballot_w64(wb <= wg));
+        if (k == 0) break;
+        found = base + k - 1;
+        if (k < 64) break;
     }
-    return lo;
+    return found;
 }
 
 // Grouped launches: XCD x (blocks b with b % 8 == x) runs its own tile range
@@ -469,7 +477,7 @@ __global__ __launch_bounds__(64 * WM *WN) void gemm_grouped_kernel(const Problem
     const int x = (int)(blockIdx.x % kXcds);
     const int64_t wg = split.begin[x] + (int64_t)(blockIdx.x / kXcds);
     if (wg >= split.begin[x + 1]) return;
-    const int i = find_gemm_problem(entries, count, wg);
+    const int i = find_gemm_problem(entries, split.first[x], split.first[x + 1], wg);
     const Problem p = entries[i];
     gemm_workgroup<MF, NF, WM, WN, MaxBufs>(p, wg - p.wg_begin, lds);
 }
@@ -556,10 +564,11 @@ hipError_t launch_gemm(const Problem &p, int variant, hipStream_t st) {
 
 int64_t gemm_xcd_schedule(Problem *entries, int count, XcdSplit *split) {
     // whole products to XCDs, largest first, each to the least loaded XCD;
-    // a product costs its tiles times (K-tiles + 1)
+    // a product costs its tiles times (K-tiles + 2): a workgroup's start and
+    // end take about as long as two K-tiles
     std::vector<int> idx(count), xcd(count);
     for (int i = 0; i < count; ++i) idx[i] = i;
-    auto cost = [&](int i) { return (int64_t)entries[i].tiles_m * entries[i].tiles_n * (entries[i].kg + 1); };
+    auto cost = [&](int i) { return (int64_t)entries[i].tiles_m * entries[i].tiles_n * (entries[i].kg + 2); };
     std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return cost(a) > cost(b); });
     int64_t load[kXcds] = {0};
     for (int i : idx) {
@@ -580,6 +589,7 @@ int64_t gemm_xcd_schedule(Problem *entries, int count, XcdSplit *split) {
             if (xcd[i] == x) mine.push_back(i);
         std::stable_sort(mine.begin(), mine.end(), [&](int a, int b) { return entries[a].kg > entries[b].kg; });
         split->begin[x] = (int32_t)tiles;
+        split->first[x] = (int32_t)out.size();
         const int64_t t0 = tiles;
         for (int i : mine) {
             Problem p = entries[i];
@@ -590,6 +600,7 @@ int64_t gemm_xcd_schedule(Problem *entries, int count, XcdSplit *split) {
         if (tiles - t0 > widest) widest = tiles - t0;
     }
     split->begin[kXcds] = (int32_t)tiles;
+    split->first[kXcds] = (int32_t)out.size();
     for (int i = 0; i < count; ++i) entries[i] = out[i];
     return widest * kXcds;
 }

@@ -34,10 +34,12 @@ struct Problem {
 enum Kind : int32_t { kKindGemv = 0, kKindGemm = 1 };
 
 // Prefill launches: the output tiles of XCD x (blocks b with b % 8 == x)
-// are tiles [begin[x], begin[x + 1]) of the launch.
+// are tiles [begin[x], begin[x + 1]) of the launch, and they belong to
+// products [first[x], first[x + 1]) of the launch's entries.
 constexpr int kXcdCount = 8;
 struct XcdSplit {
     int32_t begin[kXcdCount + 1];
+    int32_t first[kXcdCount + 1];
 };
 
 struct PlanLaunch {
@@ -49,7 +51,6 @@ struct PlanLaunch {
     int64_t lds;             // dynamic LDS bytes (gemv launches)
     int64_t sched_off;       // decode launches: byte offset of the workgroup table
     XcdSplit split;          // prefill launches
-    int32_t pad_;
 };
 
 // Decode kernel schedule: workgroup w runs batches [b0, b1) (a batch is 4
