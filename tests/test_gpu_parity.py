@@ -153,6 +153,39 @@ def test_grouped_plan_matches_single_calls_bitwise():
         assert ok, (err, mx)
 
 
+@pytest.mark.parametrize("band,bs", [((65, 208), 32), ((65, 208), 64), ((2, 16), 32), ((17, 64), 64),
+                                     ((209, 420), 32)])
+def test_grouped_tiles_across_products(band, bs):
+    """Many products of one tile shape in one plan, so that each XCD's range
+    holds several and a workgroup's consecutive tiles cross from one product
+    to the next (different K, N not always a multiple of 8, odd tile
+    counts): bit-equal to single calls and within tolerance of the oracle."""
+    rng = np.random.default_rng(band[0] * 7 + bs)
+    ks = [128, 384, 640, 1024, 2176, 96 if bs == 32 else 192]
+    specs = []
+    for i in range(30):
+        m = int(rng.integers(band[0], band[1] + 1))
+        n = int(rng.choice([64, 100, 200, 256, 520, 777]))
+        k = int(ks[i % len(ks)])
+        specs.append((m, n, k, 1000 + i))
+    problems, singles, refs = [], [], []
+    for m, n, k, seed in specs:
+        w, x = synth.random_case(seed, m, n, k, "f16")
+        q, s, zp, qw, pz = quantize_oracle(w, bs, np.float16)
+        pw = upload_packed(qw, s, pz, n, k, bs)
+        xd = torch.from_numpy(x).to(DEV)
+        problems.append((xd, pw, None))
+        singles.append(mnb.mnb_gemm(xd, pw))
+        refs.append((x, q, zp, s))
+    plan = mnb.mnb_plan_grouped(problems, bs, torch.float16)
+    outs = mnb.mnb_gemm_grouped(plan)
+    torch.cuda.synchronize()
+    for (m, n, k, _), y, ys, (x, q, zp, s) in zip(specs, outs, singles, refs):
+        assert torch.equal(y, ys), (m, n, k)
+        ok, err, mx = oracle.within_tolerance(y.cpu().numpy(), oracle.matmul_nbits(x, q, zp, s, bs), 2e-3)
+        assert ok, (m, n, k, err, mx)
+
+
 def test_repeated_calls_are_deterministic():
     w, x = synth.random_case(3, 410, 512, 2048, "f16")
     q, s, zp, qw, pz = quantize_oracle(w, 32, np.float16)
