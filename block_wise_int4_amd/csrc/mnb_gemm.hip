@@ -62,6 +62,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 #ifndef MNB_GEMM_PIPE
 #define MNB_GEMM_PIPE 5  // A-fragment reads kept in flight ahead of the MFMAs that use them
 #endif
+#ifndef MNB_GEMM_PRIO
+// A wave's issue priority is raised while it runs a stage (its MFMAs and
+// the next slice's dequantization) and lowered at the stage barrier, so
+// that a workgroup in its start or end does not take issue slots from one
+// in its K-loop: 0 never, 1 around each step's MFMAs, 2 per stage (1-2%
+// faster at M = 1500 and M = 62; 1 was slower at M = 410).
+#define MNB_GEMM_PRIO 2
+#endif
 #ifndef MNB_GEMM_STAGE_SLICES
 #define MNB_GEMM_STAGE_SLICES 4  // k-slices per LDS stage: 4 (a whole 128-input tile) or 2 (64 inputs)
 #endif
@@ -324,15 +332,24 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
             else put_pair(Rn, 0, k / 4, k % 4, dst);
         };
         h8 ring[R];
+#if MNB_GEMM_PRIO == 2
+        __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
         for (int i = 0; i < R; ++i) ring[i] = frag(i);
 #pragma unroll
         for (int q = 0; q < S * MF; ++q) {
             const int tt = q / MF, a = q % MF, t = h * S + tt;
             const h8 av = ring[q % R];
+#if MNB_GEMM_PRIO == 1
+            __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
             for (int b = 0; b < NF; ++b)
                 acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, (t & 1) ? s1[b] : s0[b], acc[a][b], 0, 0, 0);
+#if MNB_GEMM_PRIO == 1
+            __builtin_amdgcn_s_setprio(0);
+#endif
             if (q + R < S * MF) ring[q % R] = frag(q + R);
             if (a < kPieces) piece(t, a);
             if (a == MF - 1) {  // pieces the slice had no step left for
@@ -341,6 +358,9 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+#if MNB_GEMM_PRIO == 2
+        __builtin_amdgcn_s_setprio(0);
+#endif
     };
     // (after the last K-tile Rn holds no weights; its slice is formed and never used)
     auto tile = [&](int64_t c, const BRaw<NF> &Rc, BRaw<NF> &Rn) {
