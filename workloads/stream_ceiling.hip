@@ -1,0 +1,96 @@
+// Practical HBM ceilings of the box, as context for the rooflines of the
+// HBM-bound kernels: plain grid-stride streams with one 16-byte access per
+// lane per step over 2 GiB (well past the 256 MB last-level cache).
+//   read      every thread reads and folds its pieces into one word
+//   write     every thread writes its pieces
+//   read1:2   reads 512 MiB, writes 1 GiB (the embedding gather's mix:
+//             one int8 byte in, one float16 out)
+// Built by __graft_entry__.build() to workloads/_build/stream_ceiling; by hand:
+//   hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops \
+//       workloads/stream_ceiling.hip -o workloads/_build/stream_ceiling
+// then run workloads/_build/stream_ceiling on one MI355X.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+#define CHECK(x)                                                               \
+    do {                                                                       \
+        hipError_t e_ = (x);                                                   \
+        if (e_ != hipSuccess) {                                                \
+            fprintf(stderr, "%s: %s\n", #x, hipGetErrorString(e_));            \
+            exit(1);                                                           \
+        }                                                                      \
+    } while (0)
+
+__global__ __launch_bounds__(256) void stream_read(const u32x4 *__restrict__ p, size_t n, unsigned *__restrict__ out) {
+    const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    unsigned acc = 0;
+    for (size_t i = tid; i < n; i += stride) {
+        const u32x4 v = p[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    out[tid] = acc;
+}
+
+__global__ __launch_bounds__(256) void stream_write(u32x4 *__restrict__ p, size_t n) {
+    const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = tid; i < n; i += stride) p[i] = u32x4{(unsigned)i, 1u, 2u, 3u};
+}
+
+// src[0, n) in, dst[0, 2n) out
+__global__ __launch_bounds__(256) void stream_read1_write2(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
+                                                           size_t n) {
+    const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = tid; i < n; i += stride) {
+        const u32x4 v = src[i];
+        dst[2 * i] = v;
+        dst[2 * i + 1] = v + 1u;
+    }
+}
+
+template <typename F>
+static double time_ms(F launch, int reps) {
+    hipEvent_t a, b;
+    CHECK(hipEventCreate(&a));
+    CHECK(hipEventCreate(&b));
+    for (int w = 0; w < 3; ++w) launch();
+    CHECK(hipGetLastError());
+    CHECK(hipEventRecord(a));
+    for (int r = 0; r < reps; ++r) launch();
+    CHECK(hipEventRecord(b));
+    CHECK(hipEventSynchronize(b));
+    float ms = 0;
+    CHECK(hipEventElapsedTime(&ms, a, b));
+    CHECK(hipEventDestroy(a));
+    CHECK(hipEventDestroy(b));
+    return ms / reps;
+}
+
+int main() {
+    const size_t bytes = (size_t)2 << 30;
+    const size_t n = bytes / 16;
+    const int reps = 20;
+    const int max_blocks = 4096;
+    u32x4 *d;
+    unsigned *out;
+    CHECK(hipMalloc(&d, bytes));
+    CHECK(hipMemset(d, 1, bytes));
+    CHECK(hipMalloc(&out, (size_t)max_blocks * 256 * sizeof(unsigned)));
+    for (int blocks : {1024, 2048, 4096}) {
+        const double r = time_ms([&] { stream_read<<<blocks, 256>>>(d, n, out); }, reps);
+        const double w = time_ms([&] { stream_write<<<blocks, 256>>>(d, n); }, reps);
+        // 512 MiB source, 1 GiB destination, disjoint parts of the buffer
+        const double rw = time_ms([&] { stream_read1_write2<<<blocks, 256>>>(d, d + n / 4, n / 4); }, reps);
+        printf("blocks %5d  read %6.0f GB/s  write %6.0f GB/s  read1:write2 %6.0f GB/s\n", blocks,
+               bytes / (r * 1e-3) / 1e9, bytes / (w * 1e-3) / 1e9, (bytes / 4 * 3) / (rw * 1e-3) / 1e9);
+    }
+    CHECK(hipFree(d));
+    CHECK(hipFree(out));
+    return 0;
+}
