@@ -186,6 +186,30 @@ def test_grouped_tiles_across_products(band, bs):
         assert ok, (m, n, k, err, mx)
 
 
+def test_calls_run_on_the_current_stream():
+    """Products issued under a side stream run there: after that stream alone
+    is synchronized, their outputs equal the default stream's bit for bit."""
+    m, n, k = 410, 512, 2048
+    w, x = synth.random_case(31, m, n, k, "f16")
+    q, s, zp, qw, pz = quantize_oracle(w, 32, np.float16)
+    pw = upload_packed(qw, s, pz, n, k, 32)
+    xd = torch.from_numpy(x).to(DEV)
+    ref_mm = mnb.mnb_gemm(xd, pw)
+    ref_mv = mnb.mnb_gemv(xd[0].contiguous(), pw)
+    plan = mnb.mnb_plan_grouped([(xd, pw, None), (xd[:1].contiguous(), pw, None)], 32, torch.float16)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        y_mm = mnb.mnb_gemm(xd, pw)
+        y_mv = mnb.mnb_gemv(xd[0].contiguous(), pw)
+        outs = mnb.mnb_gemm_grouped(plan)
+    side.synchronize()
+    assert torch.equal(y_mm, ref_mm)
+    assert torch.equal(y_mv, ref_mv)
+    assert torch.equal(outs[0], ref_mm)
+    assert torch.equal(outs[1].reshape(-1), ref_mv)
+
+
 def test_repeated_calls_are_deterministic():
     w, x = synth.random_case(3, 410, 512, 2048, "f16")
     q, s, zp, qw, pz = quantize_oracle(w, 32, np.float16)
