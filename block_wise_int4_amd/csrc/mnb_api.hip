@@ -39,15 +39,18 @@ int prepare_product(const void *x, const void *packed, const void *y, int64_t m,
     if (m <= 0 || m > MNB_MAX_ROWS) return MNB_ERR_SHAPE;
     if (!aligned16(x) || !aligned16(packed) || !aligned16(y)) return MNB_ERR_ALIGN;
     Problem p = make_problem(x, packed, const_cast<void *>(y), m, n, k, bs, dtype_bytes(dtype));
+    // (a launch's workgroup count must fit the 32-bit grid, and stays below 2^31)
     if (dtype == MNB_F16 && m >= 2) {
         *kind = kKindGemm;
         *variant = gemm_variant(m);
         gemm_tiles(p, *variant, &p.tiles_m, &p.tiles_n);
+        if ((int64_t)p.tiles_m * p.tiles_n > 0x7FFFFFFFLL) return MNB_ERR_SHAPE;
     } else {
         *kind = kKindGemv;
         *variant = gemv_variant(dtype, m);
         if (*variant == 2 && p.kg * kTileK > gemv_max_kpad(2)) *variant = 3;
         if (p.kg * kTileK > gemv_max_kpad(*variant)) return MNB_ERR_SHAPE;
+        if (*variant >= 2 && gemv_workgroups(p, *variant) > 0x7FFFFFFFLL) return MNB_ERR_SHAPE;
     }
     *out = p;
     return MNB_OK;

@@ -77,7 +77,9 @@ typedef enum mnb_status {
     MNB_ERR_INVALID = 9    /* any other invalid argument                     */
 } mnb_status;
 
-/* Limits checked by the entry points (MNB_ERR_SHAPE beyond them). */
+/* Limits checked by the entry points (MNB_ERR_SHAPE beyond them). A product
+ * is also rejected when its kernel would need more than 2^31 - 1
+ * workgroups (an M x N output beyond about 2^44 elements). */
 #define MNB_MAX_K 32768            /* inputs per row                         */
 #define MNB_MAX_ROWS 0x7FFFFFF0LL  /* M and N                                */
 

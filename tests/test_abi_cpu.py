@@ -117,6 +117,9 @@ def test_invalid_arguments_are_rejected_before_launch(L, call, status):
 
 
 def test_k_limit(L):
+    # a product whose tile grid would not fit a launch is rejected, not wrapped
+    assert L.mnb_gemm(FAKE, FAKE2, FAKE3, 0x7FFFFFF0, 0x7FFFFFF0, 64, 4, 32, 1, None) == SHAPE
+    assert L.mnb_gemm(FAKE, FAKE2, FAKE3, 0x7FFFFFF0, 0x7FFFFFF0, 64, 4, 32, 0, None) == SHAPE
     # K up to MNB_MAX_K = 32768 inputs for both dtypes
     assert L.mnb_gemv(FAKE, FAKE2, FAKE3, 64, 32768 + 32, 4, 32, 0, None) == SHAPE
     assert L.mnb_gemm(FAKE, FAKE2, FAKE3, 4, 64, 32768 + 64, 4, 64, 1, None) == SHAPE
