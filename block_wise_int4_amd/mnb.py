@@ -99,6 +99,19 @@ def _dev(t, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _check_buf(t, name, dtype, numel, device):
+    """A caller-provided buffer the kernels read or write whole: its dtype,
+    size and device must match (contiguity is checked by _dev)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, {numel} expected")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, not {device}")
+
+
 def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -144,6 +157,11 @@ def mnb_quantize_rtn(w, block_size, dtype, bits=4, out=None, symmetric=False):
                torch.empty((N, max(nb, 1)), dtype=dtype, device=w.device),
                None if symmetric else torch.empty((N, max((nb + 1) // 2, 1)), dtype=torch.uint8, device=w.device))
     q, s, z = out
+    if block_size in (32, 64, 128) and K % block_size == 0 and K % 2 == 0:
+        _check_buf(q, "qweight", torch.uint8, N * K // 2, w.device)
+        _check_buf(s, "scales", dtype, N * nb, w.device)
+        if z is not None:
+            _check_buf(z, "zero_points", torch.uint8, N * ((nb + 1) // 2), w.device)
     _check("mnb_quantize_rtn", lib().mnb_quantize_rtn(
         _dev(w, "w"), N, K, bits, block_size, dtype_code(dtype),
         _dev(q, "qweight"), _dev(s, "scales"), None if z is None else _dev(z, "zero_points"), _stream(w.device)))
@@ -156,6 +174,12 @@ def mnb_pack(qweight, scales, zero_points, N, K, block_size, bits=4, packed=None
     dtype = scales.dtype
     zp_arg = (lambda: None) if zero_points is None else (lambda: _dev(zero_points, "zero_points"))
     nbytes = mnb_packed_bytes(N, K, block_size, dtype, bits)
+    if nbytes:
+        nb = K // block_size
+        _check_buf(qweight, "qweight", torch.uint8, N * K // 2, qweight.device)
+        _check_buf(scales, "scales", dtype, N * nb, qweight.device)
+        if zero_points is not None:
+            _check_buf(zero_points, "zero_points", torch.uint8, N * ((nb + 1) // 2), qweight.device)
     if nbytes == 0:
         # invalid format: let the library name the error (it returns before
         # touching the GPU, so a placeholder output address is never used)
@@ -198,6 +222,8 @@ def _check_x(x, pw, name="x"):
         raise ValueError(f"{name} dtype {x.dtype} differs from the weight's {pw.dtype}")
     if x.shape[-1] != pw.K:
         raise ValueError(f"{name} has {x.shape[-1]} inputs, the weight {pw.K}")
+    if pw.packed.device != x.device:
+        raise ValueError(f"the weight is on {pw.packed.device}, {name} on {x.device}")
 
 
 def mnb_gemv(x, pw, y=None):
@@ -207,6 +233,7 @@ def mnb_gemv(x, pw, y=None):
         raise ValueError("mnb_gemv takes one activation row")
     if y is None:
         y = torch.empty(pw.N, dtype=pw.dtype, device=x.device)
+    _check_buf(y, "y", pw.dtype, pw.N, x.device)
     _check("mnb_gemv", lib().mnb_gemv(
         _dev(x, "x"), _dev(pw.packed, "packed"), _dev(y, "y"), pw.N, pw.K, pw.bits, pw.block_size,
         dtype_code(pw.dtype), _stream(x.device)))
@@ -233,8 +260,11 @@ def mnb_gemv_argmax(x, pw, workspace, y=None, index=None, logits=False):
         raise ValueError("workspace: a device buffer from argmax_workspace()")
     if y is None and logits:
         y = torch.empty(pw.N, dtype=pw.dtype, device=x.device)
+    if y is not None:
+        _check_buf(y, "y", pw.dtype, pw.N, x.device)
     if index is None:
         index = torch.empty(1, dtype=torch.int64, device=x.device)
+    _check_buf(index, "index", torch.int64, 1, x.device)
     _check("mnb_gemv_argmax", lib().mnb_gemv_argmax(
         _dev(x, "x"), _dev(pw.packed, "packed"), None if y is None else _dev(y, "y"), _dev(index, "index"),
         _dev(workspace, "workspace"), pw.N, pw.K, pw.bits, pw.block_size, dtype_code(pw.dtype),
@@ -255,6 +285,9 @@ def mnb_embed_gather(table, row_scales, ids, dtype=torch.float16, out=None):
     T = ids.numel()
     if out is None:
         out = torch.empty((T, H), dtype=dtype, device=table.device)
+    _check_buf(out, "out", out.dtype, T * H, table.device)
+    if row_scales.device != table.device or ids.device != table.device:
+        raise ValueError("table, row_scales and ids must be on one device")
     _check("mnb_embed_gather", lib().mnb_embed_gather(
         _dev(table, "table"), _dev(row_scales, "row_scales"), _dev(ids, "ids"), T, V, H, dtype_code(out.dtype),
         _dev(out, "out"), _stream(table.device)))
@@ -269,6 +302,7 @@ def mnb_gemm(x, pw, y=None):
     M = x.shape[0]
     if y is None:
         y = torch.empty((M, pw.N), dtype=pw.dtype, device=x.device)
+    _check_buf(y, "y", pw.dtype, M * pw.N, x.device)
     _check("mnb_gemm", lib().mnb_gemm(
         _dev(x, "x"), _dev(pw.packed, "packed"), _dev(y, "y"), M, pw.N, pw.K, pw.bits, pw.block_size,
         dtype_code(pw.dtype), _stream(x.device)))
@@ -291,8 +325,18 @@ def mnb_plan_grouped(problems, block_size, dtype, device=None, bits=4):
         raise MnbError("mnb_plan_bytes", 8, "count out of range")
     arr = (mnb_problem * count)()
     outs, keep = [], []
-    for i, (x, pw, y) in enumerate(problems):
+    device = torch.device(device) if device is not None else problems[0][0].device
+    if device.type == "cuda" and device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    for i, (x, pw, y) in enumerate(problems):      # every problem checked before any is marshalled
         _check_x(x, pw)
+        if (pw.block_size, pw.dtype, pw.bits) != (block_size, dtype, bits):
+            raise ValueError(f"problem {i}: the weight's format differs from the plan's")
+        if x.device != device:
+            raise ValueError(f"problem {i}: x is on {x.device}, the plan on {device}")
+        if y is not None:
+            _check_buf(y, f"y[{i}]", pw.dtype, (1 if x.dim() == 1 else x.shape[0]) * pw.N, x.device)
+    for i, (x, pw, y) in enumerate(problems):
         M = 1 if x.dim() == 1 else x.shape[0]
         if y is None:
             y = torch.empty((M, pw.N), dtype=pw.dtype, device=x.device)
@@ -303,7 +347,7 @@ def mnb_plan_grouped(problems, block_size, dtype, device=None, bits=4):
     host = torch.empty(nbytes, dtype=torch.uint8)
     _check("mnb_plan_grouped", lib().mnb_plan_grouped(arr, count, bits, block_size, dtype_code(dtype),
                                                       ctypes.c_void_p(host.data_ptr()), nbytes))
-    dev = host.to(device or problems[0][0].device)
+    dev = host.to(device)
     return Plan(host, dev, outs, keep)
 
 
