@@ -84,7 +84,9 @@ struct GemmCfg {
     static constexpr int kStagesPerTile = 4 / kSlices;
     static constexpr int kLines = WM * MF * kSlices;  // 1 KB lines per stage
     static constexpr int kLinesPerWave = (kLines + kWaves - 1) / kWaves;
-    static constexpr int kStageBytes = kLines * 1024;
+    // every wave issues kLinesPerWave lines; those past kLines load zeros
+    // into padding, so that each wave's count of loads in flight is fixed
+    static constexpr int kStageBytes = kLinesPerWave * kWaves * 1024;
     // per wave, two tile groups' metadata of its NF row groups: float16
     // scales (up to 64 entries x 8 tiles = 1 KB) and zero points (256 B)
     static constexpr int kMetaScaleBytes = 1024, kMetaZpBytes = 256;
@@ -93,6 +95,8 @@ struct GemmCfg {
     // (at most MaxBufs: 2 or 3)
     static constexpr int kBufs = MaxBufs >= 3 && 3 * kStageBytes + kMetaBytes <= 160 * 1024 ? 3 : 2;
     static_assert(kSlices == 2 || kSlices == 4, "a stage holds 2 or 4 k-slices");
+    // a stage's steps 1, 2, ... issue the lines of the stage ahead, one each
+    static_assert(kLinesPerWave < kSlices * MF || kSlices * MF == 1, "a step for every line");
     static constexpr int kMetaOff = kBufs * kStageBytes;
     // epilogue staging: each wave's (MF * 16) x (NF * 16) float16 block
     static constexpr int kOutStride = NF * 32 + 16;
@@ -134,11 +138,20 @@ __device__ __forceinline__ void wait_vmem() {
 #endif
 }
 
+// Where a stage's activation lines go and how many of its inputs lie before K.
+struct LineDst {
+    uint8_t *buf;
+    uint32_t soff;  // byte offset of the stage's first input in a row
+    int32_t lim;    // K minus the stage's first input (large when no tail)
+};
+
 template <int NF>
 struct BRaw {
     u32x4 codes[NF];
     uint32_t s[NF];  // float16 scale bits of the lane's block
-    uint32_t z[NF];  // its zero point (low nibble)
+    uint32_t z[NF];  // the byte holding its zero point
+    uint32_t zsh;    // the zero point's shift in that byte (0 or 4; the same for every lane)
+    __device__ __forceinline__ uint32_t zp(int b) const { return (z[b] >> zsh) & 15u; }
 };
 
 template <int MF, int NF, int WM, int WN, int MaxBufs>
@@ -167,22 +180,26 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
         const int a = L / C::kSlices, tt = L % C::kSlices;
         voff[i] = (uint32_t)(((a * 16 + r) * p.k + j * kChunk + tt * 8) * 2);
     }
-    const bool k_tail = (p.k % kTileK) != 0;
-    auto issue_a = [&](int64_t stage) {
+    // A line piece starting at input (stage's first) + j * 32 + slice * 8
+    // reads zeros when that input is at or past K (only in the last K-tile).
+    const int jk = j * kChunk;
+    auto line_dst = [&](int64_t stage) {
         const int64_t c = stage / C::kStagesPerTile;
         const int h = (int)(stage % C::kStagesPerTile);
-        const uint32_t soff = (uint32_t)((c * kTileK + h * C::kSlices * 8) * 2);
-        uint8_t *buf = lds + (int)((uint32_t)stage % (uint32_t)C::kBufs) * C::kStageBytes;
-        const bool last = k_tail && c == p.kg - 1;
+        const int64_t first = c * kTileK + h * C::kSlices * 8;
+        const int64_t left = p.k - first;
+        return LineDst{lds + (int)((uint32_t)stage % (uint32_t)C::kBufs) * C::kStageBytes, (uint32_t)(first * 2),
+                       (int32_t)(left < kTileK ? left : 0x40000000)};
+    };
+    auto issue_line = [&](const LineDst &d, int i) {
+        const int L = wave + i * C::kWaves;
+        const uint32_t vo = L >= C::kLines || jk >= d.lim - (L % C::kSlices) * 8 ? kOob : voff[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)(d.buf + L * 1024), 16, vo, d.soff, 0, 0);
+    };
+    auto issue_a = [&](int64_t stage) {
+        const LineDst d = line_dst(stage);
 #pragma unroll
-        for (int i = 0; i < C::kLinesPerWave; ++i) {
-            const int L = wave + i * C::kWaves;
-            if (L < C::kLines) {
-                uint32_t vo = voff[i];
-                if (last && c * kTileK + j * kChunk + (h * C::kSlices + L % C::kSlices) * 8 >= p.k) vo = kOob;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void *)(buf + L * 1024), 16, vo, soff, 0, 0);
-            }
-        }
+        for (int i = 0; i < C::kLinesPerWave; ++i) issue_line(d, i);
     };
 
     // ---- weight metadata: tile group G of this wave's row groups -> LDS ----
@@ -197,54 +214,55 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
 #pragma unroll
         for (int b = 0; b < NF; ++b) {
             const int64_t g = g0 + wn * NF + b;
-            if (g < p.rg) {
-                const int64_t mi = meta_index(g, p.nbt, p.kgp, 0, G * kMetaGroup);
-                const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
-                    const_cast<uint8_t *>(p.packed + p.scales_off + mi * 2), 0, E * kMetaGroup * 2, 0x00020000);
-                const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
-                    const_cast<uint8_t *>(p.packed + p.zp_off + mi / 2), 0, E * kMetaGroup / 2, 0x00020000);
-                const uint32_t so = (uint32_t)lane * 16u, zo = (uint32_t)lane * 4u;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void *)meta_s(slot, b), 16, so, 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(zr, (lds_void *)meta_z(slot, b), 4, zo, 0, 0, 0);
-            }
+            const bool in = g < p.rg;
+            const int64_t mi = meta_index(in ? g : 0, p.nbt, p.kgp, 0, G * kMetaGroup);
+            const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t *>(p.packed + p.scales_off + mi * 2), 0, in ? E * kMetaGroup * 2 : 0, 0x00020000);
+            const __amdgpu_buffer_rsrc_t zr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t *>(p.packed + p.zp_off + mi / 2), 0, in ? E * kMetaGroup / 2 : 0, 0x00020000);
+            const uint32_t so = (uint32_t)lane * 16u, zo = (uint32_t)lane * 4u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void *)meta_s(slot, b), 16, so, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(zr, (lds_void *)meta_z(slot, b), 4, zo, 0, 0, 0);
         }
     };
 
     // ---- weight tiles -------------------------------------------------------
+    // (a row group past N has an empty range: its codes read as zero)
+    __amdgpu_buffer_rsrc_t code_rsrc[NF];
+#pragma unroll
+    for (int b = 0; b < NF; ++b) {
+        const int64_t g = g0 + wn * NF + b;
+        const bool in = g < p.rg;
+        code_rsrc[b] = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(p.packed + (in ? g : 0) * p.kg * kTileCodeBytes), 0,
+            in ? (int)(p.kg * kTileCodeBytes) : 0, 0x00020000);
+    }
     auto load_codes = [&](int64_t c, BRaw<NF> &R) {
 #pragma unroll
-        for (int b = 0; b < NF; ++b) {
-            const int64_t g = g0 + wn * NF + b;
-            if (g < p.rg)
-                R.codes[b] = *(reinterpret_cast<const u32x4 *>(p.packed + (g * p.kg + c) * kTileCodeBytes) + lane);
-            else
-                R.codes[b] = u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int b = 0; b < NF; ++b)
+            R.codes[b] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(code_rsrc[b], (int)(c * kTileCodeBytes) + lane * 16, 0, 0));
     };
+    // (the nibble is taken out where it is used, so that nothing waits for
+    // these reads until then)
     auto read_meta = [&](int64_t c, BRaw<NF> &R) {
         const int slot = (int)((c / kMetaGroup) & 1), u = (int)(c % kMetaGroup);
+        R.zsh = 4u * (uint32_t)(u & 1);
 #pragma unroll
         for (int b = 0; b < NF; ++b) {
-            const int64_t g = g0 + wn * NF + b;
-            if (g < p.rg) {
-                R.s[b] = *reinterpret_cast<const uint16_t *>(meta_s(slot, b) + e * 16 + u * 2);
-                R.z[b] = (uint32_t)meta_z(slot, b)[e * 4 + (u >> 1)] >> (4 * (u & 1));
-            } else {
-                R.s[b] = 0u;
-                R.z[b] = 0u;
-            }
+            const bool in = g0 + wn * NF + b < p.rg;
+            const uint32_t sv = *reinterpret_cast<const uint16_t *>(meta_s(slot, b) + e * 16 + u * 2);
+            const uint32_t zv = meta_z(slot, b)[e * 4 + (u >> 1)];
+            R.s[b] = in ? sv : 0u;
+            R.z[b] = in ? zv : 0u;
         }
-    };
-    auto load_b = [&](int64_t c, BRaw<NF> &R) {
-        load_codes(c, R);
-        read_meta(c, R);
     };
     // B operands of slice t (inputs t*8 .. t*8+7 of the lane's chunk)
     auto dequant_t = [&](const BRaw<NF> &R, int t, h8 (&out)[NF]) {
 #pragma unroll
         for (int b = 0; b < NF; ++b) {
             const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)R.s[b]);
-            const h2 zm = zp_magic(R.z[b] & 15u);
+            const h2 zm = zp_magic(R.zp(b));
             const h2 s2 = {s, s};
             const u32x4 w = R.codes[b];
             const uint32_t word = w[t];
@@ -266,25 +284,15 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
         for (int b = 0; b < NF; ++b) acc[a][b] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int64_t n_stages = C::kStagesPerTile * p.kg;
-    // a wave may own one line fewer than kLinesPerWave; it waits for its own count
-    const bool full_lines = wave + (C::kLinesPerWave - 1) * C::kWaves < C::kLines;
     // the next stage's lines must have landed; those two stages ahead may
     // still be in flight (each wave waits for its own loads, then the barrier)
     auto stage_sync = [&](int64_t stage) {
         if (C::kBufs == 3 && stage + 2 < n_stages) {
-            if (full_lines) wait_vmem<C::kLinesPerWave>();
-            else wait_vmem<C::kLinesPerWave - 1>();
+            wait_vmem<C::kLinesPerWave>();
         } else {
             wait_vmem<0>();
         }
         __syncthreads();
-    };
-    auto issue_ahead = [&](int64_t stage) {
-        if (C::kBufs == 3) {
-            if (stage + 2 < n_stages) issue_a(stage + 2);
-        } else if (stage + 1 < n_stages) {
-            issue_a(stage + 1);
-        }
     };
 
     // Tile c: slices 0..3 in 4 / kSlices stages. Weights of tile c + 1 are
@@ -307,7 +315,7 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     // the same exact (q - zp) pair times the scale as dequant_pair_f16
     auto put_pair = [&](const BRaw<NF> &R, int t, int b, int hh, h8 &dst) {
         const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)R.s[b]);
-        const h2 zm = zp_magic(R.z[b] & 15u);
+        const h2 zm = zp_magic(R.zp(b));
         const h2 s2 = {s, s};
         const u32x4 w = R.codes[b];
         const uint32_t word = hh ? w[t] >> (4 * hh) : w[t];
@@ -318,7 +326,7 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     // Stage `stage` (stage h of its tile: slices h*kSlices .. + kSlices - 1):
     // each step forms one pair of the next slice's B operands, from Rc, or
     // from Rn (the next tile's slice 0) after the tile's last slice.
-    auto run_stage = [&](int64_t stage, auto h_tag, const BRaw<NF> &Rc, const BRaw<NF> &Rn) {
+    auto run_stage = [&](int64_t stage, auto h_tag, const BRaw<NF> &Rc, const BRaw<NF> &Rn, auto &&step_hook) {
         constexpr int h = decltype(h_tag)::value;
         constexpr int S = C::kSlices;
         constexpr int R = MNB_GEMM_PIPE < S * MF ? MNB_GEMM_PIPE : S * MF;
@@ -351,6 +359,7 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
             __builtin_amdgcn_s_setprio(0);
 #endif
             if (q + R < S * MF) ring[q % R] = frag(q + R);
+            step_hook(q);
             if (a < kPieces) piece(t, a);
             if (a == MF - 1) {  // pieces the slice had no step left for
 #pragma unroll
@@ -362,18 +371,30 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
         __builtin_amdgcn_s_setprio(0);
 #endif
     };
+    // Each stage's steps 1, 2, ... issue one activation line each of the
+    // stage ahead, where the MFMAs around them cover their issue. Every wave
+    // issues the same loads in every tile (past the last stage the lines
+    // read zeros into the free buffer), so the compiler's count of the loads
+    // in flight is exact wherever it waits for the next tile's codes and
+    // never falls back to waiting for all of them.
     // (after the last K-tile Rn holds no weights; its slice is formed and never used)
     auto tile = [&](int64_t c, const BRaw<NF> &Rc, BRaw<NF> &Rn) {
-        const bool more = c + 1 < p.kg;
-        if (c % kMetaGroup == 0 && c / kMetaGroup + 1 < n_groups) issue_meta(c / kMetaGroup + 1);
-        if (more) load_b(c + 1, Rn);
         const int64_t st = C::kStagesPerTile * c;
-        issue_ahead(st);
-        run_stage(st, std::integral_constant<int, 0>{}, Rc, Rn);
+        if (c % kMetaGroup == 0 && c / kMetaGroup + 1 < n_groups) issue_meta(c / kMetaGroup + 1);
+        if (c + 1 < p.kg) {
+            load_codes(c + 1, Rn);
+            read_meta(c + 1, Rn);
+        }
+        const LineDst d = line_dst(st + (C::kBufs == 3 ? 2 : 1));
+        run_stage(st, std::integral_constant<int, 0>{}, Rc, Rn, [&](int q) {
+            if (q >= 1 && q <= C::kLinesPerWave) issue_line(d, q - 1);
+        });
         stage_sync(st);
         if constexpr (C::kStagesPerTile == 2) {
-            issue_ahead(st + 1);
-            run_stage(st + 1, std::integral_constant<int, 1>{}, Rc, Rn);
+            const LineDst d1 = line_dst(st + (C::kBufs == 3 ? 3 : 2));
+            run_stage(st + 1, std::integral_constant<int, 1>{}, Rc, Rn, [&](int q) {
+                if (q >= 1 && q <= C::kLinesPerWave) issue_line(d1, q - 1);
+            });
             stage_sync(st + 1);
         }
     };
@@ -385,6 +406,7 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
         R1.s[b] = 0u;
         R1.z[b] = 0u;
     }
+    R1.zsh = 0u;
     // metadata, codes and lines of the first K-tile all in flight at once;
     // the metadata is issued first (pinned by a scheduling barrier), since
     // the wait below counts the loads issued after it
@@ -394,16 +416,14 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     load_codes(0, R0);
     issue_a(0);
     if (two) issue_a(1);
-    // tile group 0's metadata has landed once at most one code load and the
-    // lines are pending (a wave with metadata issued a code load after it,
-    // and at least kLinesPerWave - 1 lines per stage)
-    if (two) wait_vmem<1 + 2 * (C::kLinesPerWave - 1)>();
-    else wait_vmem<1 + C::kLinesPerWave - 1>();
+    // tile group 0's metadata has landed once at most the codes and the
+    // lines are pending
+    if (two) wait_vmem<NF + 2 * C::kLinesPerWave>();
+    else wait_vmem<NF + C::kLinesPerWave>();
     read_meta(0, R0);
     dequant_t(R0, 0, s0);
     if (two) {
-        if (full_lines) wait_vmem<C::kLinesPerWave>();
-        else wait_vmem<C::kLinesPerWave - 1>();
+        wait_vmem<C::kLinesPerWave>();
     } else {
         wait_vmem<0>();
     }
