@@ -304,22 +304,36 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     // multiplies from slot t & 1).
     h8 s0[NF], s1[NF];
     const int64_t n_groups = (p.kg + kMetaGroup - 1) / kMetaGroup;
-    // The nibble mask and the 1024 offset held in registers (literal
-    // constants cannot go into the three-operand form), so that masking a
-    // pair and adding the offset is one v_and_or_b32.
-    uint32_t pair_mask = 0x000F000Fu, pair_magic = 0x64006400u;
+    // Pairs hh = 0 and 2 (nibbles at bits 0 and 16, after a shift by 8 for
+    // hh = 2) become 1024 + q under the 0x6400 exponent, whose ulp is 1;
+    // pairs hh = 1 and 3 sit 4 bits higher and become 64 + q under 0x5400,
+    // whose ulp is 1/16, with no shift. Subtracting 1024 + zp or 64 + zp
+    // leaves the same exact q - zp, times the scale with one rounding (the
+    // value dequant_pair_f16 forms). The masks and offsets are held in
+    // registers (literal constants cannot go into the three-operand form),
+    // so that masking a pair and adding the offset is one v_and_or_b32.
+    uint32_t pair_mask = 0x000F000Fu, pair_mask_hi = 0x00F000F0u, pair_magic = 0x64006400u, pair_magic_hi = 0x54005400u;
 #if defined(__HIP_DEVICE_COMPILE__)
     asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(pair_mask));
+    asm volatile("s_mov_b32 %0, 0x00f000f0" : "=s"(pair_mask_hi));
     asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(pair_magic));
+    asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(pair_magic_hi));
 #endif
-    // the same exact (q - zp) pair times the scale as dequant_pair_f16
     auto put_pair = [&](const BRaw<NF> &R, int t, int b, int hh, h8 &dst) {
         const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)R.s[b]);
-        const h2 zm = zp_magic(R.zp(b));
+        const uint32_t zp = R.zp(b);
         const h2 s2 = {s, s};
         const u32x4 w = R.codes[b];
-        const uint32_t word = hh ? w[t] >> (4 * hh) : w[t];
-        const h2 d = (as_h2((word & pair_mask) | pair_magic) - zm) * s2;
+        const uint32_t word = hh >= 2 ? w[t] >> 8 : w[t];
+        h2 x, zm;
+        if (hh & 1) {
+            x = as_h2((word & pair_mask_hi) | pair_magic_hi);
+            zm = as_h2(0x54005400u | (zp << 4) | (zp << 20));
+        } else {
+            x = as_h2((word & pair_mask) | pair_magic);
+            zm = zp_magic(zp);
+        }
+        const h2 d = (x - zm) * s2;
         dst[2 * hh] = d.x;
         dst[2 * hh + 1] = d.y;
     };
