@@ -114,7 +114,9 @@ GEMM_CASES = [(2, 64, 64, 32), (7, 200, 256, 32), (16, 1024, 2048, 32), (17, 96,
               # one K-tile (with and without a ragged tail) and K-loops shorter or a little longer than
               # each tile shape's ring of prefetched code tiles
               (40, 64, 128, 32), (48, 200, 96, 32), (70, 100, 128, 32), (60, 130, 384, 64), (64, 256, 640, 32),
-              (12, 100, 896, 32), (16, 64, 2176, 32), (30, 70, 1152, 64), (62, 3072, 1024, 64)]
+              (12, 100, 896, 32), (16, 64, 2176, 32), (30, 70, 1152, 64), (62, 3072, 1024, 64),
+              # the 208- and 192-row tiles with a ragged K tail and a partial last N-tile
+              (200, 130, 2112, 64), (300, 520, 1184, 32), (100, 300, 4160, 32), (250, 130, 96, 32)]
 
 
 @pytest.mark.parametrize("m,n,k,bs", GEMM_CASES)
