@@ -21,7 +21,7 @@ inline int dtype_bytes(int dtype) { return dtype == MNB_F16 ? 2 : 4; }
 // Format and shape checks common to every entry point.
 int check_format(int64_t n, int64_t k, int bits, int bs, int dtype) {
     if (bits != 4) return MNB_ERR_BITS;
-    if (bs != 32 && bs != 64 && bs != 128) return MNB_ERR_BLOCK;
+    if (bs != 32 && bs != 64 && bs != 128 && bs != 256) return MNB_ERR_BLOCK;
     if (dtype != MNB_F32 && dtype != MNB_F16) return MNB_ERR_DTYPE;
     if (n <= 0 || k <= 0 || k % bs != 0) return MNB_ERR_SHAPE;
     if (n > MNB_MAX_ROWS || k > MNB_MAX_K) return MNB_ERR_SHAPE;
@@ -67,7 +67,7 @@ const char *mnb_status_string(int status) {
     case MNB_OK: return "ok";
     case MNB_ERR_NULL: return "a required pointer is NULL";
     case MNB_ERR_BITS: return "bits must be 4";
-    case MNB_ERR_BLOCK: return "block_size must be 32, 64 or 128";
+    case MNB_ERR_BLOCK: return "block_size must be 32, 64, 128 or 256";
     case MNB_ERR_SHAPE: return "invalid shape (M, N, K > 0, K a multiple of block_size, within limits)";
     case MNB_ERR_DTYPE: return "unsupported dtype";
     case MNB_ERR_ALIGN: return "device pointer not 16-byte aligned";

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void pack_meta_kernel(const T *__restrict__ sc
     uint32_t zbyte = 0;
     for (int h = 0; h < 2; ++h) {
         const int64_t c = 2 * cp + h;
-        const int64_t b = c * L.nbt + jb;
+        const int64_t b = c * kTileK / L.bs + jb;  // the block of entry jb of tile c
         T s = (T)0.0f;
         uint32_t z = 0;
         if (n < L.n && c < L.kg && b < nb) {

@@ -15,7 +15,8 @@
 //
 // Scales and zero points. Within a tile, row r has nbt = 128 / block_size
 // blocks; entry e = jb * 16 + r names block jb of row r (lane l reads entry
-// (j / (block_size / 32)) * 16 + r). Tiles are taken in groups of 8 (kgp =
+// (j / (block_size / 32)) * 16 + r). A 256-input block spans two tiles:
+// nbt is 1 and both tiles' entries hold that block's scale and zero point. Tiles are taken in groups of 8 (kgp =
 // kg rounded up to 8), and for each (row group, tile group) the metadata is
 // one contiguous block, entry-major: entry e holds its 8 tiles' values in
 // tile order. A lane therefore reads the scales of 8 consecutive tiles with
@@ -51,8 +52,8 @@ struct Layout {
     int64_t n, k;        // logical shape
     int64_t rg, kg;      // tile rows (N_pad / 16), tile columns (K_pad / 128)
     int64_t kgp;         // kg rounded up to a multiple of 8 (metadata stride)
-    int bs;              // block size (32 or 64)
-    int nbt;             // blocks per row per tile: 128 / bs
+    int bs;              // block size (32, 64, 128 or 256)
+    int nbt;             // metadata entries per row per tile: 128 / bs, at least 1
     int scale_bytes;     // 2 or 4
     int64_t scales_off;  // byte offsets inside the packed buffer
     int64_t zp_off;
@@ -67,7 +68,7 @@ MNB_HD Layout make_layout(int64_t n, int64_t k, int bs, int scale_bytes) {
     L.kg = (k + kTileK - 1) / kTileK;
     L.kgp = align_up(L.kg, kMetaGroup);
     L.bs = bs;
-    L.nbt = kTileK / bs;
+    L.nbt = bs >= kTileK ? 1 : kTileK / bs;
     L.scale_bytes = scale_bytes;
     const int64_t entries = L.rg * L.nbt * kTileRows;  // metadata entries over all row groups
     L.scales_off = align_up(L.rg * L.kg * kTileCodeBytes, kAlign);

@@ -157,7 +157,7 @@ def mnb_quantize_rtn(w, block_size, dtype, bits=4, out=None, symmetric=False):
                torch.empty((N, max(nb, 1)), dtype=dtype, device=w.device),
                None if symmetric else torch.empty((N, max((nb + 1) // 2, 1)), dtype=torch.uint8, device=w.device))
     q, s, z = out
-    if block_size in (32, 64, 128) and K % block_size == 0 and K % 2 == 0:
+    if block_size in (32, 64, 128, 256) and K % block_size == 0 and K % 2 == 0:
         _check_buf(q, "qweight", torch.uint8, N * K // 2, w.device)
         _check_buf(s, "scales", dtype, N * nb, w.device)
         if z is not None:

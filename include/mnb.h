@@ -24,7 +24,7 @@
  *    are reentrant. Calls on one stream run in order.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call that touches device memory is asynchronous on it.
- *  - bits must be 4, block_size 32, 64 or 128, K a positive multiple of
+ *  - bits must be 4, block_size 32, 64, 128 or 256, K a positive multiple of
  *    block_size, M and N positive.
  *  - dtype is the activation dtype, which is also the scale dtype and the
  *    output dtype: MNB_F32 or MNB_F16. Accumulation is float32.
@@ -66,7 +66,7 @@ typedef enum mnb_status {
     MNB_OK = 0,
     MNB_ERR_NULL = 1,      /* a required pointer is NULL                     */
     MNB_ERR_BITS = 2,      /* bits != 4                                      */
-    MNB_ERR_BLOCK = 3,     /* block_size not 32, 64 or 128                   */
+    MNB_ERR_BLOCK = 3,     /* block_size not 32, 64, 128 or 256              */
     MNB_ERR_SHAPE = 4,     /* M, N, K <= 0, K % block_size != 0, or a size
                               beyond the documented limits                    */
     MNB_ERR_DTYPE = 5,     /* dtype not MNB_F32 / MNB_F16, or not supported

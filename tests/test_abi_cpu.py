@@ -46,7 +46,7 @@ def _expected_bytes(n, k, bs, sb):
         return (v + a - 1) // a * a
     rg, kg = math.ceil(n / 16), math.ceil(k / 128)
     kgp = math.ceil(kg / 8) * 8           # per-entry metadata padded to 8 tiles
-    entries = rg * (128 // bs) * 16
+    entries = rg * max(1, 128 // bs) * 16   # a 256-input block: one entry per tile
     codes = up(rg * kg * 1024)
     scales = up(codes + entries * kgp * sb)
     return up(scales + entries * kgp // 2)
@@ -54,7 +54,7 @@ def _expected_bytes(n, k, bs, sb):
 
 @pytest.mark.parametrize("n,k,bs,dt", [(3072, 1024, 32, 0), (151936, 1024, 32, 1), (768, 3072, 64, 1),
                                        (17, 96, 32, 1), (1, 32, 32, 0), (5, 64, 64, 1), (2048, 1024, 128, 1),
-                                       (33, 384, 128, 0)])
+                                       (33, 384, 128, 0), (100, 512, 256, 1), (16, 256, 256, 0)])
 def test_packed_bytes(L, n, k, bs, dt):
     assert L.mnb_packed_bytes(n, k, 4, bs, dt) == _expected_bytes(n, k, bs, 4 if dt == 0 else 2)
 
@@ -67,7 +67,8 @@ def test_packed_bytes_equal_algorithmic_bytes_on_whole_tiles(L):
 
 
 @pytest.mark.parametrize("args", [(0, 64, 4, 32, 1), (4, 0, 4, 32, 1), (4, 48, 4, 32, 1), (4, 64, 3, 32, 1),
-                                  (4, 64, 4, 16, 1), (4, 64, 4, 32, 2), (4, 65536, 4, 32, 1)])
+                                  (4, 64, 4, 16, 1), (4, 64, 4, 32, 2), (4, 65536, 4, 32, 1), (4, 128, 4, 256, 1),
+                                  (4, 512, 4, 512, 1)])
 def test_packed_bytes_invalid_is_zero(L, args):
     assert L.mnb_packed_bytes(*args) == 0
 
@@ -90,7 +91,8 @@ ODD = ctypes.c_void_p((1 << 20) + 8)
     (lambda L: L.mnb_gemm(FAKE, FAKE2, ODD, 8, 64, 64, 4, 32, 1, None), ALIGN),
     (lambda L: L.mnb_gemm(FAKE, FAKE2, FAKE3, 8, 64, 40000, 4, 32, 1, None), SHAPE),
     (lambda L: L.mnb_pack(None, FAKE2, None, 64, 64, 4, 32, 1, FAKE3, None), NULL),
-    (lambda L: L.mnb_pack(FAKE, FAKE2, None, 64, 64, 4, 256, 1, FAKE3, None), BLOCK),
+    (lambda L: L.mnb_pack(FAKE, FAKE2, None, 64, 512, 4, 512, 1, FAKE3, None), BLOCK),
+    (lambda L: L.mnb_pack(FAKE, FAKE2, None, 64, 384, 4, 256, 1, FAKE3, None), SHAPE),
     (lambda L: L.mnb_pack(FAKE, FAKE2, None, 64, 64, 4, 16, 1, FAKE3, None), BLOCK),
     (lambda L: L.mnb_quantize_rtn(FAKE, 64, 64, 4, 32, 1, FAKE2, None, None, None), NULL),
     (lambda L: L.mnb_gemv(FAKE, FAKE2, FAKE3, 64, 192, 4, 128, 1, None), SHAPE),

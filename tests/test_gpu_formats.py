@@ -1,6 +1,6 @@
 """GPU: the format variants - symmetric weights (no zero points, fixed zero
-point 8) and block size 128 - through quantize, pack, unpack, dequant and
-the products, against the oracle (bit-exact for codes, scales, zero points
+point 8) and block sizes 128 and 256 (a block spanning two 128-input tiles) -
+through quantize, pack, unpack, dequant and the products, against the oracle (bit-exact for codes, scales, zero points
 and dequantized weights; outputs within the usual tolerance)."""
 
 import numpy as np
@@ -33,8 +33,9 @@ def _oracle(w, bs, dt, symmetric):
     return (oracle.rtn_quantize_symmetric if symmetric else oracle.rtn_quantize)(w, bs, dt)
 
 
-FORMATS = [(True, 32), (True, 64), (True, 128), (False, 128)]
-SHAPES = [(64, 256), (17, 384), (1, 128), (40, 4224)]
+FORMATS = [(True, 32), (True, 64), (True, 128), (False, 128), (False, 256), (True, 256)]
+# (9, 768): an odd number of 256-blocks per row, so the last zero-point byte is half padding
+SHAPES = [(64, 256), (17, 384), (1, 128), (40, 4224), (9, 768), (33, 2560)]
 
 
 @pytest.mark.parametrize("dt", [np.float16, np.float32])
