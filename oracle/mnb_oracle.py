@@ -6,8 +6,8 @@ blocking, fusion or reordering beyond what each definition states.
 
 Notation, following the model-card pages ("Mega-ASR INT4 ONNX", section
 "Conversion details"; "Qwen3-ASR-0.6B ONNX for the browser", section "Pick a
-variant"): a weight W has N output rows and K inputs; blocks of `bs` (32, 64
-or 128) consecutive inputs of one row share one scale `s` and one 4-bit zero
+variant"): a weight W has N output rows and K inputs; blocks of `bs` (32, 64,
+128 or 256) consecutive inputs of one row share one scale `s` and one 4-bit zero
 point `zp`; codes `q` are 4-bit unsigned. MatMulNBits computes
 Y[M, N] = X[M, K] @ D[N, K]^T with D = (q - zp) * s.
 

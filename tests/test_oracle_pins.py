@@ -241,7 +241,8 @@ def _check_nearest_grid(w, q, s, zp, bs):
                     assert (c - z) % 2 == 0
 
 
-@pytest.mark.parametrize("dtype,bs", [(np.float16, 32), (np.float32, 32), (np.float16, 64), (np.float32, 64)])
+@pytest.mark.parametrize("dtype,bs", [(np.float16, 32), (np.float32, 32), (np.float16, 64), (np.float32, 64),
+                                      (np.float16, 256)])
 def test_rtn_codes_are_nearest_grid_points(dtype, bs):
     rng = np.random.default_rng(13)
     w = (rng.standard_normal((4, 2 * bs)) * 0.02).astype(np.float32)
@@ -249,7 +250,7 @@ def test_rtn_codes_are_nearest_grid_points(dtype, bs):
     _check_nearest_grid(w, q, s, zp, bs)
 
 
-@pytest.mark.parametrize("dtype,bs", [(np.float16, 32), (np.float32, 32), (np.float16, 64)])
+@pytest.mark.parametrize("dtype,bs", [(np.float16, 32), (np.float32, 32), (np.float16, 64), (np.float32, 256)])
 def test_rtn_round_trip_bound(dtype, bs):
     rng = np.random.default_rng(17)
     w = (rng.standard_normal((64, 8 * bs)) * 0.02).astype(np.float32)
@@ -463,7 +464,7 @@ def test_symmetric_tie_rounds_half_to_even_and_zero_block():
     assert float(s[1, 0]) == 0.0 and (q[1] == 8).all()
 
 
-@pytest.mark.parametrize("dtype,bs", [(np.float16, 32), (np.float32, 64), (np.float16, 128)])
+@pytest.mark.parametrize("dtype,bs", [(np.float16, 32), (np.float32, 64), (np.float16, 128), (np.float16, 256)])
 def test_symmetric_codes_are_nearest_grid_points(dtype, bs):
     rng = np.random.default_rng(bs)
     w = (rng.standard_normal((6, 2 * bs)) * 0.02).astype(np.float32)
