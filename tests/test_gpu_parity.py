@@ -134,24 +134,26 @@ def test_gemm_fp32_parity(m, n, k, bs):
     assert ok, f"max err {err:.3e} vs 1e-5 * {mx:.3e}"
 
 
-def test_grouped_plan_matches_single_calls_bitwise():
+@pytest.mark.parametrize("bs", [32, 256])
+def test_grouped_plan_matches_single_calls_bitwise(bs):
     specs = [(1, 256, 1024, 1), (1, 17, 96, 2), (410, 128, 256, 3), (33, 64, 512, 4), (1, 2048, 2048, 5),
              (1500, 64, 768, 6)]
     problems, singles, refs = [], [], []
     for m, n, k, seed in specs:
+        k = k if k % bs == 0 else bs
         w, x = synth.random_case(seed, m, n, k, "f16")
-        q, s, zp, qw, pz = quantize_oracle(w, 32, np.float16)
-        pw = upload_packed(qw, s, pz, n, k, 32)
+        q, s, zp, qw, pz = quantize_oracle(w, bs, np.float16)
+        pw = upload_packed(qw, s, pz, n, k, bs)
         xd = torch.from_numpy(x).to(DEV)
         problems.append((xd, pw, None))
         singles.append(mnb.mnb_gemm(xd, pw))
         refs.append((x, q, zp, s))
-    plan = mnb.mnb_plan_grouped(problems, 32, torch.float16)
+    plan = mnb.mnb_plan_grouped(problems, bs, torch.float16)
     outs = mnb.mnb_gemm_grouped(plan)
     torch.cuda.synchronize()
     for y, ys, (x, q, zp, s) in zip(outs, singles, refs):
         assert torch.equal(y, ys)
-        ok, err, mx = oracle.within_tolerance(y.cpu().numpy(), oracle.matmul_nbits(x, q, zp, s, 32), 2e-3)
+        ok, err, mx = oracle.within_tolerance(y.cpu().numpy(), oracle.matmul_nbits(x, q, zp, s, bs), 2e-3)
         assert ok, (err, mx)
 
 
