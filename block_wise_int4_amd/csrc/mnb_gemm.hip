@@ -30,9 +30,9 @@
 // Instruction order. A stage runs as one fixed sequence (pinned with
 // scheduling barriers): each step issues a fragment's MFMAs, the LDS read of
 // the fragment MNB_GEMM_PIPE steps later into a small register ring, and one
-// float16 pair of the next slice's weights. The compiler's own order, under
-// this kernel's register pressure, left each read one step ahead and
-// waited for every read.
+// or two float16 pairs of the next slice's weights. The compiler's own
+// order, under this kernel's register pressure, left each read one step
+// ahead and waited for every read.
 //
 // Activation side: an LDS stage holds one whole 128-input tile of the
 // workgroup's rows (MNB_GEMM_STAGE_SLICES = 4; 2 splits it in two stages of
@@ -374,10 +374,15 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
 #endif
             if (q + R < S * MF) ring[q % R] = frag(q + R);
             step_hook(q);
-            if (a < kPieces) piece(t, a);
+            // pairs per step: 2 for the small-M tiles (16 pairs per slice
+            // over 1-4 steps), 1 for the tall ones (8 pairs over 12-13 steps)
+            constexpr int P = NF >= 4 ? 2 : 1;
+#pragma unroll
+            for (int u = 0; u < P; ++u)
+                if (a * P + u < kPieces) piece(t, a * P + u);
             if (a == MF - 1) {  // pieces the slice had no step left for
 #pragma unroll
-                for (int k = MF; k < kPieces; ++k) piece(t, k);
+                for (int k = MF * P; k < kPieces; ++k) piece(t, k);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
