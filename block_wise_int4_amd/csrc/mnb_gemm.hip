@@ -17,10 +17,10 @@
 // lane and fragment (lane l holds row l & 15, chunk l >> 4: 32 codes). The
 // scales and zero points of its row groups reach LDS once per 8 tiles by
 // direct buffer-to-LDS loads (one contiguous span per row group and tile
-// group), and each tile's values are read from there. MFMA k-slice t (t = 0..3) uses inputs
-// t*8 .. t*8+7 of the lane's chunk: the lane turns that word into exact
-// (q - zp) float16 pairs with the 1024-offset trick and multiplies them by
-// the scale with one rounding (the helper mnb_dequant uses, so the MFMA
+// group), and each tile's values are read from there. MFMA k-slice t
+// (t = 0..3) uses inputs t*8 .. t*8+7 of the lane's chunk: the lane turns
+// that word into exact (q - zp) float16 pairs with the 1024- and 64-offset
+// tricks and multiplies them by the scale with one rounding (the helper mnb_dequant uses, so the MFMA
 // operands are exactly the dequantized weights). The sum over K does not
 // care which inputs an MFMA groups together as long as A and B agree, so A
 // is laid out with the same grouping and no lane shuffles are needed on
@@ -40,7 +40,9 @@
 // byte 16*l of a line holds the 8 inputs lane l passes to that MFMA, so
 // every A read is one conflict-free ds_read_b128 of a contiguous kilobyte.
 // The lines are filled by buffer_load_dwordx4 ... lds, whose 64 lanes write
-// 64 consecutive 16-byte slots: each lane loads the piece its slot needs.
+// 64 consecutive 16-byte slots: each lane loads the piece its slot needs;
+// the lines of the stage ahead are issued one per step from inside the
+// current stage's MFMA steps.
 // Rows past M and inputs past K fall outside the buffer's range and read as
 // zero. Two stage buffers (three where they fit) let the loads run one
 // stage (two) ahead, with one barrier per stage; a whole-tile stage halves
