@@ -25,7 +25,9 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call that touches device memory is asynchronous on it.
  *  - bits must be 4, block_size 32, 64, 128 or 256, K a positive multiple of
- *    block_size, M and N positive.
+ *    block_size, M and N positive. The pages use 32 and 64; 128 and 256 are
+ *    format variants (a 256-input block spans two of the layout's 128-input
+ *    tiles), with the same formula.
  *  - dtype is the activation dtype, which is also the scale dtype and the
  *    output dtype: MNB_F32 or MNB_F16. Accumulation is float32.
  *  - Every argument is checked on the host before anything is enqueued; on
