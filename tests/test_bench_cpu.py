@@ -1,0 +1,91 @@
+"""Host-side logic of bench.py that needs no GPU: the one-GPU refusal, and
+the HBM-traffic bookkeeping (counter calibration against a plain device copy,
+bytes per launch, records tied to the kernel sources they were taken on)."""
+
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, value in rows:
+            w.writerow({"Kernel_Name": name, "Counter_Name": counter, "Counter_Value": value})
+
+
+def test_record_traffic_calibrates_each_counter_on_the_copy(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    probe_mib = 512
+    copy_kib = probe_mib * 1024
+    # FETCH_SIZE reads half of the copied bytes, WRITE_SIZE all of them; two
+    # launches of each kernel are averaged; a smaller copy is not the probe
+    fetch = tmp_path / "fetch.csv"
+    write = tmp_path / "write.csv"
+    _counter_csv(fetch, "FETCH_SIZE", [("__amd_rocclr_copyBuffer", copy_kib / 2), ("__amd_rocclr_copyBuffer", 10.0),
+                                       ("mnb::decode_grouped_kernel<...>", 1000.0),
+                                       ("mnb::decode_grouped_kernel<...>", 1200.0),
+                                       ("void mnb::gemm_grouped_kernel<13, 2>", 4000.0)])
+    _counter_csv(write, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", copy_kib), ("mnb::decode_grouped_kernel<...>", 8.0),
+                                       ("mnb::decode_grouped_kernel<...>", 12.0),
+                                       ("void mnb::gemm_grouped_kernel<13, 2>", 300.0)])
+    workloads = {"decode_grouped_kernel": "decode-a", "gemm_grouped_kernel": "prefill-b"}
+    bench.record_traffic(str(fetch), str(write), probe_mib, workloads, "the command")
+    data = json.load(open(tmp_path / "traffic.json"))
+    dec = data["decode_grouped_kernel:decode-a"]
+    assert dec["fetch_factor"] == 2.0 and dec["write_factor"] == 1.0
+    assert dec["bytes_per_launch"] == round(1100.0 * 1024 * 2 + 10.0 * 1024)
+    assert dec["source_sha"] == bench.kernel_source_sha("decode_grouped_kernel")
+    assert dec["command"] == "the command"
+    gemm = data["gemm_grouped_kernel:prefill-b"]
+    assert gemm["bytes_per_launch"] == round(4000.0 * 1024 * 2 + 300.0 * 1024)
+    assert bench.stored_traffic("decode_grouped_kernel:decode-a") == dec["bytes_per_launch"]
+
+
+def test_record_traffic_needs_the_copy_probe(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    fetch = tmp_path / "fetch.csv"
+    write = tmp_path / "write.csv"
+    _counter_csv(fetch, "FETCH_SIZE", [("mnb::decode_grouped_kernel", 1.0)])
+    _counter_csv(write, "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 1.0)])
+    with pytest.raises(SystemExit):
+        bench.record_traffic(str(fetch), str(write), 512, {"decode_grouped_kernel": "w"}, "")
+
+
+def test_traffic_taken_on_other_sources_is_ignored(tmp_path, monkeypatch):
+    path = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
+    sha = bench.kernel_source_sha("gemm_grouped_kernel")
+    assert len(sha) == 16 and int(sha, 16) >= 0
+    json.dump({"gemm_grouped_kernel:w": {"bytes_per_launch": 7, "source_sha": sha},
+               "gemm_grouped_kernel:old": {"bytes_per_launch": 9, "source_sha": "0" * 16}}, open(path, "w"))
+    assert bench.stored_traffic("gemm_grouped_kernel:w") == 7
+    assert bench.stored_traffic("gemm_grouped_kernel:old") is None
+    assert bench.stored_traffic("gemm_grouped_kernel:absent") is None
+
+
+def test_committed_traffic_records_name_their_sources():
+    data = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+    assert data
+    for key, rec in data.items():
+        kernel = key.split(":")[0]
+        assert kernel in bench.KERNEL_SOURCES
+        assert rec["bytes_per_launch"] > 0 and rec["fetch_factor"] > 0 and rec["write_factor"] > 0
+        assert len(rec["source_sha"]) == 16 and "rocprofv3 --pmc" in rec["command"]
