@@ -10,9 +10,12 @@
 // weight.
 //
 // A wave streams its row group 8 tiles at a time: per tile one fully
-// coalesced 128-bit load per lane (row r = lane & 15, chunk j = lane >> 4),
-// and per 8 tiles one 16-byte scale load and one 4-byte zero-point load.
-// The next 8 tiles are in flight while the current ones are computed.
+// coalesced, non-temporal 128-bit load per lane (row r = lane & 15, chunk
+// j = lane >> 4), and per 8 tiles one 16-byte scale load and one 4-byte
+// zero-point load; it then computes those tiles. The CU's other waves keep
+// the memory busy meanwhile: with 12 waves per CU, also keeping the next 8
+// tiles in flight during the arithmetic measured slower (more bytes in
+// flight than HBM serves best).
 //
 // Arithmetic per 32-input chunk: (w >> 4h) & 0x000F000F places two 4-bit
 // codes in the low bits of two float16 halves with a zero exponent, i.e. the
@@ -221,8 +224,7 @@ __device__ __forceinline__ uint64_t decode_range(const Problem *entries, Problem
         int64_t sb = b, g = (b - p.batch_begin) * kGemvWaves + wave;
         int64_t c0 = 0;
         bool have = g < p.rg;
-        Group<T> cur, nxt;
-        if (have) load_group<T>(p, g, 0, lane, e, cur);
+        Group<T> cur;
         stage_x<T>(p, xs, xsum);
 
         float acc = 0.0f;
@@ -235,7 +237,7 @@ __device__ __forceinline__ uint64_t decode_range(const Problem *entries, Problem
             }
             const int64_t ng = (nb - p.batch_begin) * kGemvWaves + wave;
             const bool nvalid = nb < bend && ng < p.rg;
-            if (nvalid) load_group<T>(p, ng, nc0, lane, e, nxt);
+            load_group<T>(p, g, c0, lane, e, cur);
             acc += group_math<T>(cur, p.kg - c0, xs, xsum, c0, j);
             if (nc0 == 0) {  // row group finished
                 float v = acc;
@@ -255,7 +257,6 @@ __device__ __forceinline__ uint64_t decode_range(const Problem *entries, Problem
                 acc = 0.0f;
             }
             if (!nvalid) break;
-            cur = nxt;
             sb = nb;
             c0 = nc0;
             g = ng;
