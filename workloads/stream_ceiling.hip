@@ -1,8 +1,11 @@
 // Practical HBM ceilings of the box, as context for the rooflines of the
-// HBM-bound kernels: plain grid-stride streams with one 16-byte access per
-// lane per step over 2 GiB (well past the 256 MB last-level cache).
-//   read      every thread reads and folds its pieces into one word
-//   write     every thread writes its pieces
+// HBM-bound kernels: streams with 16-byte accesses over 2 GiB (well past the
+// 256 MB last-level cache).
+//   read      grid-stride, every thread reads and folds its pieces
+//   read nt   each workgroup reads one contiguous chunk with non-temporal
+//             loads, U pieces per lane in flight (the decode kernel's kind
+//             of access: contiguous, non-temporal); the fastest read found
+//   write     grid-stride, every thread writes its pieces
 //   read1:2   reads 512 MiB, writes 1 GiB (the embedding gather's mix:
 //             one int8 byte in, one float16 out)
 // Built by __graft_entry__.build() to workloads/_build/stream_ceiling; by hand:
@@ -34,6 +37,23 @@ __global__ __launch_bounds__(256) void stream_read(const u32x4 *__restrict__ p, 
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
     out[tid] = acc;
+}
+
+// workgroup b reads elements [b * per, (b + 1) * per), per = n / gridDim
+// rounded down to whole steps of U * 256 (so no access leaves the chunk)
+template <int U>
+__global__ __launch_bounds__(256) void stream_read_nt(const u32x4 *__restrict__ p, size_t n, unsigned *__restrict__ out) {
+    const size_t per = n / gridDim.x / (U * 256) * (U * 256);
+    const u32x4 *q = p + (size_t)blockIdx.x * per;
+    unsigned acc = 0;
+    for (size_t i = threadIdx.x; i < per; i += U * 256) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(q + i + u * 256);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
 __global__ __launch_bounds__(256) void stream_write(u32x4 *__restrict__ p, size_t n) {
@@ -82,6 +102,13 @@ int main() {
     CHECK(hipMalloc(&d, bytes));
     CHECK(hipMemset(d, 1, bytes));
     CHECK(hipMalloc(&out, (size_t)max_blocks * 256 * sizeof(unsigned)));
+    for (int blocks : {768, 1024, 1536}) {
+        const size_t per2 = n / blocks / 512 * 512, per4 = n / blocks / 1024 * 1024;
+        const double r2 = time_ms([&] { stream_read_nt<2><<<blocks, 256>>>(d, n, out); }, reps);
+        const double r4 = time_ms([&] { stream_read_nt<4><<<blocks, 256>>>(d, n, out); }, reps);
+        printf("blocks %5d  read nt, contiguous chunks: %6.0f GB/s (2 in flight)  %6.0f GB/s (4 in flight)\n", blocks,
+               per2 * blocks * 16.0 / (r2 * 1e-3) / 1e9, per4 * blocks * 16.0 / (r4 * 1e-3) / 1e9);
+    }
     for (int blocks : {1024, 2048, 4096}) {
         const double r = time_ms([&] { stream_read<<<blocks, 256>>>(d, n, out); }, reps);
         const double w = time_ms([&] { stream_write<<<blocks, 256>>>(d, n); }, reps);
