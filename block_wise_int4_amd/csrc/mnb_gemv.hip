@@ -83,9 +83,11 @@ struct Group {
     uint32_t z;
 };
 
-// Loads tiles [c0, c0 + kTG) of row group g (tiles past kg are not read).
+// Loads tiles [c0, c0 + kTG) of row group g (tiles past kg are not read);
+// mi is the metadata index of entry e of row group g, tile c0.
 template <typename T>
-__device__ __forceinline__ void load_group(const Problem &p, int64_t g, int64_t c0, int lane, int e, Group<T> &G) {
+__device__ __forceinline__ void load_group(const Problem &p, int64_t g, int64_t c0, int lane, int64_t mi,
+                                           Group<T> &G) {
     const uint8_t *base = p.packed + (g * p.kg + c0) * kTileCodeBytes + lane * 16;
     const int64_t nt = p.kg - c0;
 #pragma unroll
@@ -97,7 +99,6 @@ __device__ __forceinline__ void load_group(const Problem &p, int64_t g, int64_t 
 #endif
         else G.codes[u] = u32x4{0u, 0u, 0u, 0u};
     }
-    const int64_t mi = meta_index(g, p.nbt, p.kgp, e, c0);
     G.s.load(p.packed + p.scales_off + mi * (int64_t)sizeof(T));
     if constexpr (kTG == 8) G.z = *reinterpret_cast<const uint32_t *>(p.packed + p.zp_off + (mi >> 1));
     else G.z = *reinterpret_cast<const uint16_t *>(p.packed + p.zp_off + (mi >> 1));
@@ -108,16 +109,18 @@ template <typename T>
 __device__ __forceinline__ float group_math(const Group<T> &G, int64_t nt, const T *xs, const float *xsum, int64_t c0,
                                             int j) {
     float acc = 0.0f;
+    // the group's first tile in LDS; tile u sits at a constant offset from it
+    const T *xg = xs + c0 * kTileK + j * kChunk;
+    const float *sg = xsum + c0 * 4 + j;
 #pragma unroll
     for (int u = 0; u < kTG; ++u) {
         if (u >= nt) break;
-        const int64_t c = c0 + u;
         const float s = G.s.get(u);
-        const float zs = (float)((G.z >> (4 * u)) & 15u) * xsum[c * 4 + j];
+        const float zs = (float)((G.z >> (4 * u)) & 15u) * sg[u * 4];
         const u32x4 w = G.codes[u];
         float part = 0.0f;
         if constexpr (sizeof(T) == 2) {
-            const u32x4 *xv = reinterpret_cast<const u32x4 *>(xs + c * kTileK + j * kChunk);
+            const u32x4 *xv = reinterpret_cast<const u32x4 *>(xg + u * kTileK);
 #if MNB_DECODE_TWO_MASK
             // pairs 0 and 2 masked in place (q * 2^-24), pairs 1 and 3 masked
             // one nibble higher (q * 2^-20) into a second sum scaled back by
@@ -144,7 +147,7 @@ __device__ __forceinline__ float group_math(const Group<T> &G, int64_t nt, const
 #endif
             part = __builtin_fmaf(part, 16777216.0f, -zs);  // 2^24 undoes the subnormal scaling exactly
         } else {
-            const float4 *xv = reinterpret_cast<const float4 *>(xs + c * kTileK + j * kChunk);
+            const float4 *xv = reinterpret_cast<const float4 *>(xg + u * kTileK);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const float4 xa = xv[2 * t], xb = xv[2 * t + 1];
@@ -228,6 +231,7 @@ __device__ __forceinline__ uint64_t decode_range(const Problem *entries, Problem
         stage_x<T>(p, xs, xsum);
 
         float acc = 0.0f;
+        int64_t mi_row = 0;  // metadata index of entry e, tile 0 of row group g
         while (have) {
             // the step after this one: next 8 tiles, or the next batch's row group
             int64_t nb = sb, nc0 = c0 + kTG;
@@ -237,7 +241,9 @@ __device__ __forceinline__ uint64_t decode_range(const Problem *entries, Problem
             }
             const int64_t ng = (nb - p.batch_begin) * kGemvWaves + wave;
             const bool nvalid = nb < bend && ng < p.rg;
-            load_group<T>(p, g, c0, lane, e, cur);
+            if (c0 == 0) mi_row = meta_index(g, p.nbt, p.kgp, e, 0);
+            load_group<T>(p, g, c0, lane, mi_row + (c0 / kMetaGroup) * (p.nbt * kTileRows * kMetaGroup) + c0 % kMetaGroup,
+                          cur);
             acc += group_math<T>(cur, p.kg - c0, xs, xsum, c0, j);
             if (nc0 == 0) {  // row group finished
                 float v = acc;
