@@ -141,7 +141,16 @@ def time_steps(fn_list, steps, warmup, torch, per_launch=False):
     return start.elapsed_time(end) / steps, per
 
 
-def run_workload(cfg, steps, warmup, per_linear, torch, dev, launch_events=False):
+def leg_floor(steps, warmup, est_ms):
+    """Warm-up and timed launches for a leg that is not the headline: at
+    least 20 warm-up launches, and at least 40 timed ones or 50 ms of timed
+    work, whatever --steps says (a short timed region of a long kernel is
+    dominated by the first launches' clock ramp)."""
+    timed = max(steps, 40, math.ceil(50.0 / max(est_ms, 1e-3)))
+    return timed, max(warmup, 20)
+
+
+def run_workload(cfg, steps, warmup, per_linear, torch, dev, launch_events=False, floor=False):
     from block_wise_int4_amd import mnb, workload
 
     t0 = time.time()
@@ -160,13 +169,20 @@ def run_workload(cfg, steps, warmup, per_linear, torch, dev, launch_events=False
 
     launches = mnb.mnb_plan_launches(plans[0])
     fns = [lambda p=p: mnb.mnb_gemm_grouped(p) for p in plans]
-    ms, _ = time_steps(fns, steps, warmup, torch)
-    out = {"ms": ms, "bytes": algo, "flops": flops, "replicas": replicas, "launches_per_step": launches}
+    # the first launch of the workload on its own (cold: nothing warmed up);
+    # it counts as the first warm-up step
+    first_ms, _ = time_steps(fns[:1], 1, 0, torch)
+    if floor:
+        steps, warmup = leg_floor(steps, warmup, first_ms)
+    ms, _ = time_steps(fns, steps, max(warmup - 1, 0), torch)
+    out = {"ms": ms, "bytes": algo, "flops": flops, "replicas": replicas, "launches_per_step": launches,
+           "first_launch_ms": first_ms, "steps": steps, "warmup": warmup}
     if launches == 1:
         # the step is one launch, back to back: the region's time per step is
         # the kernel's average duration (launch to launch)
         out["launch_ms"] = ms
-    log(f"[bench] {cfg.name}: grouped {ms * 1e3:.1f} us/step ({launches} launches per step)")
+    log(f"[bench] {cfg.name}: grouped {ms * 1e3:.1f} us/step over {steps} steps after {warmup} "
+        f"({launches} launches per step; first launch {first_ms * 1e3:.1f} us)")
     if launch_events:
         _, per = time_steps(fns, steps, warmup, torch, per_launch=True)
         srt = sorted(per)
@@ -182,12 +198,64 @@ def run_workload(cfg, steps, warmup, per_linear, torch, dev, launch_events=False
                     else:
                         mnb.mnb_gemm(ld.x, ld.pw, ld.y)
             return f
+        passes = [one_pass(s) for s in sets]
         pl_steps = max(3, steps // 4)
-        out["per_linear_ms"], _ = time_steps([one_pass(s) for s in sets], pl_steps, min(warmup, 3), torch)
-        log(f"[bench] {cfg.name}: per-linear {out['per_linear_ms'] * 1e3:.1f} us/step")
+        out["per_linear_ms"], _ = time_steps(passes, pl_steps, min(warmup, 3), torch)
+        # the same calls captured once per replica set into a HIP graph and
+        # replayed: the device-side cost of one call per linear, without the
+        # host's per-call overhead
+        graphs = []
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        for f in passes:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                f()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        out["per_linear_graph_ms"], _ = time_steps([g.replay for g in graphs], max(pl_steps, 10),
+                                                   max(3, min(warmup, 10)), torch)
+        del graphs
+        log(f"[bench] {cfg.name}: per-linear {out['per_linear_ms'] * 1e3:.1f} us/step issued from the host, "
+            f"{out['per_linear_graph_ms'] * 1e3:.1f} us/step replayed from a graph")
     del plans, sets, base
     torch.cuda.empty_cache()
     return out
+
+
+def leg_record(cfg, res, kernel):
+    """JSON object for one timed workload: throughput, its roofline against
+    the bound that applies, and the per-linear schedules."""
+    mb = cfg.m > 1
+    launch_ms = res.get("launch_ms", res["ms"])
+    if mb:
+        achieved = res["flops"] / (launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "algorithmic_flops_per_launch": res["flops"]}
+    else:
+        achieved = res["bytes"] / (launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": stored_traffic(f"{kernel}:{cfg.name}"), "kernel": kernel,
+                 "launch_us": round(launch_ms * 1e3, 2),
+                 "launch_timing": "timed region / steps (one launch per step, back to back)",
+                 "algorithmic_bytes_per_launch": res["bytes"]})
+    rec = {"workload": cfg.name, "M": cfg.m, "linears": len(cfg.linears), "block_size": cfg.block_size,
+           "steps": res["steps"], "warmup": res["warmup"], "ms_per_step": round(res["ms"], 5),
+           "first_launch_us": round(res["first_launch_ms"] * 1e3, 2), "schedule": "grouped",
+           "launches_per_step": res["launches_per_step"], "replicas": res["replicas"], "roofline": roof}
+    if mb:
+        rec.update({"value": round(res["flops"] / (res["ms"] * 1e-3) / 1e12, 2), "unit": "TFLOP/s"})
+    else:
+        rec.update({"value": round(res["bytes"] / (res["ms"] * 1e-3) / 1e9, 2), "unit": "GB/s"})
+    if "per_linear_ms" in res:
+        def rate(ms):
+            return round((res["flops"] / (ms * 1e-3) / 1e12) if mb else (res["bytes"] / (ms * 1e-3) / 1e9), 2)
+        rec["per_linear"] = {"unit": rec["unit"], "host_issued_ms_per_step": round(res["per_linear_ms"], 5),
+                             "host_issued": rate(res["per_linear_ms"]),
+                             "graph_ms_per_step": round(res["per_linear_graph_ms"], 5),
+                             "graph": rate(res["per_linear_graph_ms"])}
+    return rec
 
 
 def run_lm_head_argmax(cfg, steps, warmup, torch, dev):
@@ -257,9 +325,22 @@ def run_embed_gather(cfg, steps, warmup, torch, dev, token_counts=(410, 65536)):
     return res
 
 
-def cpu_baseline(cfg, budget_s):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(cfg, budget_s, runs=3):
     """The oracle (NumPy float64 dequantize + matmul) on the host cores, on a
-    bounded prefix of the workload's linears. Quantization is not timed."""
+    bounded prefix of the workload's linears: the prefix the first pass
+    finishes within budget_s / runs, then the same prefix again, `runs`
+    passes in all. Quantization is not timed."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -267,9 +348,9 @@ def cpu_baseline(cfg, budget_s):
     from workloads import synth
 
     dt = np.float16 if cfg.dtype == "f16" else np.float32
-    done_bytes, done_flops, elapsed, used = 0, 0, 0.0, []
+    done_bytes, done_flops, first, used, sample = 0, 0, 0.0, [], []
     for lin in cfg.linears:
-        if elapsed >= budget_s:
+        if first >= budget_s / runs:
             break
         w, x = synth.linear_inputs(cfg, lin)
         n_rows = lin.n
@@ -280,17 +361,40 @@ def cpu_baseline(cfg, budget_s):
         q, s, zp = quantize(w, cfg.block_size, dt)
         t = time.perf_counter()
         oracle.matmul_nbits(x, q, zp, s, cfg.block_size)
-        elapsed += time.perf_counter() - t
+        first += time.perf_counter() - t
+        sample.append((x, q, zp, s))
         nb = lin.k // cfg.block_size
         a = 2 if cfg.dtype == "f16" else 4
         zp_bytes = 0 if cfg.symmetric else n_rows * ((nb + 1) // 2)
         done_bytes += n_rows * lin.k // 2 + n_rows * nb * a + zp_bytes + cfg.m * (lin.k + n_rows) * a
         done_flops += 2 * cfg.m * n_rows * lin.k
         used.append(f"{lin.proj}{'' if lin.layer < 0 else lin.layer}" + ("" if n_rows == lin.n else f"[:{n_rows}]"))
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"seconds": elapsed, "bytes": done_bytes, "flops": done_flops, "threads": threads,
+    times = [first]
+    for _ in range(runs - 1):
+        t = time.perf_counter()
+        for x, q, zp, s in sample:
+            oracle.matmul_nbits(x, q, zp, s, cfg.block_size)
+        times.append(time.perf_counter() - t)
+    times.sort()
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"median_s": times[len(times) // 2], "min_s": times[0], "bytes": done_bytes, "flops": done_flops,
+            "cores": len(os.sched_getaffinity(0)), "blas_threads": blas, "cpu_model": cpu_model(), "runs": runs,
             "sample": f"{len(used)} of {len(cfg.linears)} linears in order ({used[0]}..{used[-1]}), "
-                      f"{done_bytes / 1e6:.1f} MB algorithmic"}
+                      f"{done_bytes / 1e6:.1f} MB algorithmic, {done_flops / 1e9:.1f} GFLOP; {runs} passes"}
+
+
+def cpu_record(cb, mb):
+    """cpu_baseline JSON object: throughput of the median pass (and of the
+    fastest), in the workload's unit."""
+    if mb:
+        val = lambda t: round(cb["flops"] / t / 1e12, 5)  # noqa: E731
+        unit = "TFLOP/s"
+    else:
+        val = lambda t: round(cb["bytes"] / t / 1e9, 4)  # noqa: E731
+        unit = "GB/s"
+    return {"value": val(cb["median_s"]), "unit": unit, "cores": cb["cores"], "kind": "oracle",
+            "sample": cb["sample"], "best": val(cb["min_s"]), "median_s": round(cb["median_s"], 3),
+            "min_s": round(cb["min_s"], 3), "blas_threads": cb["blas_threads"], "cpu_model": cb["cpu_model"]}
 
 
 def main():
@@ -300,6 +404,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=1, help="headline workload (index into workloads.configs)")
     ap.add_argument("--prefill-config", type=int, default=3, help="prefill workload timed alongside; -1 = none")
+    ap.add_argument("--extra-configs", default="2,4",
+                    help="further workloads timed as legs of the line (comma-separated indices; '' = none)")
     ap.add_argument("--no-per-linear", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true", help="skip the LM-head argmax and embedding-gather lines")
@@ -313,8 +419,10 @@ def main():
     ap.add_argument("--traffic-command", default="", help="the profiled command, stored with --record-traffic")
     args = ap.parse_args()
 
+    from workloads import configs
+    extra = [int(c) for c in args.extra_configs.split(",") if c.strip()]
+
     if args.record_traffic:
-        from workloads import configs
         wl = {"decode_grouped_kernel": configs.CONFIGS[args.config].name,
               "gemm_grouped_kernel": configs.CONFIGS[args.prefill_config].name}
         record_traffic(*args.record_traffic, args.copy_probe_mib or 512, wl, args.traffic_command)
@@ -327,7 +435,6 @@ def main():
     import torch
 
     from block_wise_int4_amd import mnb
-    from workloads import configs
 
     if not os.path.exists(mnb.LIB_PATH):
         from block_wise_int4_amd import build as _b
@@ -349,13 +456,14 @@ def main():
         log(f"[bench] device copy of {args.copy_probe_mib} MiB: {ms_copy * 1e3:.1f} us = {copy_gbs:.0f} GB/s read+write")
         del a, b
 
+    def kernel_of(c):
+        return "decode_grouped_kernel" if c.m == 1 else "gemm_grouped_kernel"
+
+    # headline: exactly --steps timed steps after --warmup
     cfg = configs.CONFIGS[args.config]
     dec = run_workload(cfg, args.steps, args.warmup, not args.no_per_linear, torch, dev, args.launch_events)
+    head = leg_record(cfg, dec, kernel_of(cfg))
     gbs = dec["bytes"] / (dec["ms"] * 1e-3) / 1e9
-    # one launch per step: the kernel's algorithmic bytes per launch are the step's
-    k_gbs = dec["bytes"] / (dec.get("launch_ms", dec["ms"]) * 1e-3) / 1e9
-    decode_kernel = "decode_grouped_kernel" if cfg.m == 1 else "gemm_grouped_kernel"
-    dec_traffic = stored_traffic(f"{decode_kernel}:{cfg.name}")
 
     result = {
         "metric": "int4 MatMulNBits decode GB/s (M=1) & prefill TFLOP/s, % of MI355X roofline",
@@ -376,19 +484,12 @@ def main():
             "activations": cfg.dtype, "accumulate": "f32", "schedule": "grouped",
             "launches_per_step": dec["launches_per_step"], "replicas": dec["replicas"],
             "algorithmic_bytes_per_step": dec["bytes"],
-            "per_linear_ms_per_step": round(dec.get("per_linear_ms", float("nan")), 5),
-            "per_linear_GBps": round(dec["bytes"] / (dec["per_linear_ms"] * 1e-3) / 1e9, 2)
-            if "per_linear_ms" in dec else None,
+            "first_launch_us": head["first_launch_us"],
         },
-        "roofline": {
-            "bound": "hbm", "achieved": round(k_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(k_gbs / HBM_PEAK_GBS, 4),
-            "traffic": dec_traffic,
-            "kernel": decode_kernel, "launch_us": round(dec.get("launch_ms", dec["ms"]) * 1e3, 2),
-            "launch_timing": "timed region / steps (one launch per step, back to back)",
-            "algorithmic_bytes_per_launch": dec["bytes"],
-        },
+        "roofline": head["roofline"],
     }
+    if "per_linear" in head:
+        result["config"]["per_linear"] = head["per_linear"]
 
     if any(l.proj == "lm_head" for l in cfg.linears) and not args.no_next:
         result["lm_head_argmax"] = run_lm_head_argmax(cfg, args.steps, args.warmup, torch, dev)
@@ -396,40 +497,26 @@ def main():
 
     if args.prefill_config >= 0:
         pcfg = configs.CONFIGS[args.prefill_config]
-        pre = run_workload(pcfg, max(5, args.steps // 10), max(2, args.warmup // 10), not args.no_per_linear,
-                           torch, dev, args.launch_events)
-        tf = pre["flops"] / (pre["ms"] * 1e-3) / 1e12
-        k_tf = pre["flops"] / (pre.get("launch_ms", pre["ms"]) * 1e-3) / 1e12
-        result["prefill"] = {
-            "workload": pcfg.name, "M": pcfg.m, "linears": len(pcfg.linears), "value": round(tf, 2),
-            "unit": "TFLOP/s", "ms_per_step": round(pre["ms"], 5), "schedule": "grouped",
-            "launches_per_step": pre["launches_per_step"],
-            "per_linear_TFLOPs": round(pre["flops"] / (pre["per_linear_ms"] * 1e-3) / 1e12, 2)
-            if "per_linear_ms" in pre else None,
-            "roofline": {"bound": "mfma", "achieved": round(k_tf, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(k_tf / MFMA_F16_PEAK_TFLOPS, 4),
-                         "traffic": stored_traffic(f"gemm_grouped_kernel:{pcfg.name}"),
-                         "kernel": "gemm_grouped_kernel",
-                         "launch_us": round(pre.get("launch_ms", pre["ms"]) * 1e3, 2),
-                         "launch_timing": "timed region / steps (one launch per step, back to back)",
-                         "algorithmic_flops_per_launch": pre["flops"]},
-        }
+        pre = run_workload(pcfg, args.steps, args.warmup, not args.no_per_linear, torch, dev, args.launch_events,
+                           floor=True)
+        result["prefill"] = leg_record(pcfg, pre, kernel_of(pcfg))
+
+    legs = {}
+    for ci in extra:
+        ecfg = configs.CONFIGS[ci]
+        res = run_workload(ecfg, args.steps, args.warmup, not args.no_per_linear, torch, dev, args.launch_events,
+                           floor=True)
+        legs[ecfg.name] = leg_record(ecfg, res, kernel_of(ecfg))
+    if legs:
+        result["legs"] = legs
 
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline: oracle on {cfg.name} (budget {args.cpu_budget:.0f}s)")
-        cb = cpu_baseline(cfg, args.cpu_budget)
-        result["cpu_baseline"] = {
-            "value": round(cb["bytes"] / cb["seconds"] / 1e9, 4), "unit": "GB/s",
-            "cores": cb["threads"], "kind": "oracle", "sample": cb["sample"],
-        }
+        result["cpu_baseline"] = cpu_record(cpu_baseline(cfg, args.cpu_budget), cfg.m > 1)
         if args.prefill_config >= 0:
             pcfg = configs.CONFIGS[args.prefill_config]
             log(f"[bench] cpu baseline: oracle on {pcfg.name}")
-            pb = cpu_baseline(pcfg, args.cpu_budget)
-            result["prefill"]["cpu_baseline"] = {
-                "value": round(pb["flops"] / pb["seconds"] / 1e12, 5), "unit": "TFLOP/s",
-                "cores": pb["threads"], "kind": "oracle", "sample": pb["sample"],
-            }
+            result["prefill"]["cpu_baseline"] = cpu_record(cpu_baseline(pcfg, args.cpu_budget), True)
 
     print(json.dumps(result), flush=True)
 

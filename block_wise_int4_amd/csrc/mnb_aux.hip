@@ -127,8 +127,11 @@ __global__ __launch_bounds__(256) void pack_meta_kernel(const T *__restrict__ sc
 }
 
 // ---------------------------------------------------------------------------
-// Read-back exports, one thread per code slot, through the same helpers the
-// compute kernels use (code_at / dequant_pair_f16 / dequant_f32).
+// Read-back exports, one thread per code slot. They run the helpers the
+// compute kernels run: unpack reads each code through the decode kernel's
+// subnormal pair form (and the float32 paths' code_at must agree with it),
+// dequant forms float16 weights with the MFMA kernel's dequant pair form
+// and float32 weights with dequant_f32.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t *__restrict__ packed, Layout L,
                                                      uint8_t *__restrict__ q, uint8_t *__restrict__ zp) {
@@ -144,8 +147,19 @@ __global__ __launch_bounds__(256) void unpack_kernel(const uint8_t *__restrict__
     if (n >= L.n || k0 >= L.k) return;
     const uint4 v = *reinterpret_cast<const uint4 *>(packed + tile * kTileCodeBytes + l * 16);
     const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-    for (int t = 0; t < 4; ++t)
-        for (int u = 0; u < 8; ++u) q[n * L.k + k0 + 8 * t + u] = (uint8_t)code_at(wv[t], u);
+    for (int t = 0; t < 4; ++t) {
+        for (int h = 0; h < 4; ++h) {
+            // the pair as the decode kernel's dot products see it, scaled back
+            const h2 sub = as_h2(subnormal_pair(wv[t], wv[t] >> 8, h));
+            const float unscale = (h & 1) ? kSubnormalUnscale * kHighPairScale : kSubnormalUnscale;
+            const uint32_t c0 = (uint32_t)((float)sub.x * unscale), c1 = (uint32_t)((float)sub.y * unscale);
+            // code_at (the float32 kernels' reader) names the same codes, or the
+            // slot reads 0xFF, which no valid code equals
+            const bool agree = c0 == code_at(wv[t], 2 * h) && c1 == code_at(wv[t], 2 * h + 1);
+            q[n * L.k + k0 + 8 * t + 2 * h] = agree ? (uint8_t)c0 : 0xFFu;
+            q[n * L.k + k0 + 8 * t + 2 * h + 1] = agree ? (uint8_t)c1 : 0xFFu;
+        }
+    }
     const int chunks_per_block = L.bs / kChunk;
     if (j % chunks_per_block == 0) {
         const int e = (j / chunks_per_block) * kTileRows + r;
@@ -175,11 +189,11 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
     const uint32_t z = (packed[L.zp_off + (mi >> 1)] >> (4 * (mi & 1))) & 15u;
     T *dst = w + n * L.k + k0;
     if constexpr (sizeof(T) == 2) {
-        const h2 zm = zp_magic(z);
         const h2 s2 = {s, s};
+        const PairForm pf = pair_form_literal();
         for (int t = 0; t < 4; ++t)
             for (int h = 0; h < 4; ++h) {
-                const h2 d = dequant_pair_f16(wv[t], h, zm, s2);
+                const h2 d = dequant_pair_f16(wv[t], h, z, s2, pf);
                 dst[8 * t + 2 * h] = d.x;
                 dst[8 * t + 2 * h + 1] = d.y;
             }

@@ -38,34 +38,61 @@ __host__ __device__ __forceinline__ uint32_t to_canonical_word(uint32_t d) {
     return c;
 }
 
-// Float16 pair (1024 + q_2h, 1024 + q_2h+1) from device word w, pair h (0..3):
-// 0x6400 is 1024.0 in float16, whose unit in the last place is 1, so OR-ing
-// a 4-bit integer into the low mantissa bits adds it exactly.
-__device__ __forceinline__ uint32_t magic_pair(uint32_t w, int h) {
-    return ((w >> (4 * h)) & 0x000F000Fu) | 0x64006400u;
+// ---------------------------------------------------------------------------
+// Pair forms. Inputs 2h and 2h+1 (h = 0..3) of a device word sit at bits 4h
+// and 4h + 16, so pairs h = 0 and 2 land in the low nibble of each 16-bit
+// half (after a shift by 8 for h = 2) and pairs h = 1 and 3 one nibble
+// higher. Each form below takes a pair out with one mask and no per-pair
+// shift; the kernels run these helpers and nothing else, and the read-back
+// exports (mnb_unpack, mnb_dequant) run them too, so their bit-exact tests
+// check the code the products execute.
+// ---------------------------------------------------------------------------
+
+// Masks and float16 offsets of the dequant pair form. The MFMA kernel pins
+// them in registers (three-operand v_and_or_b32 takes no literal), other
+// callers use the literals.
+struct PairForm {
+    uint32_t mask_lo, mask_hi;    // 0x000F000F, 0x00F000F0
+    uint32_t magic_lo, magic_hi;  // 0x6400 = 1024.0 (ulp 1), 0x5400 = 64.0 (ulp 1/16), in both halves
+};
+__device__ __forceinline__ PairForm pair_form_literal() {
+    return PairForm{0x000F000Fu, 0x00F000F0u, 0x64006400u, 0x54005400u};
 }
 
-// The same offset form of a zero point, in both halves.
-__device__ __forceinline__ h2 zp_magic(uint32_t zp) { return as_h2(0x64006400u | zp | (zp << 16)); }
-
-// Exact float16 pair (q - zp) for inputs (2h, 2h+1): both operands lie in
-// [1024, 1039], so their difference is an exactly representable integer.
-__device__ __forceinline__ h2 centered_pair(uint32_t w, int h, h2 zm) { return as_h2(magic_pair(w, h)) - zm; }
-
-// Dequantized float16 pair: the exact (q - zp) times the scale, one rounding
-// (round half to even) in the float16 multiply.
-__device__ __forceinline__ h2 dequant_pair_f16(uint32_t w, int h, h2 zm, h2 s2) {
-    return centered_pair(w, h, zm) * s2;
+// Dequantized float16 pair h of device word w. Pairs h = 0, 2 become
+// 1024 + q under the 0x6400 exponent (whose ulp is 1); pairs h = 1, 3,
+// masked in place, become 64 + q under 0x5400 (ulp 1/16). Subtracting the
+// zero point in the same offset form (1024 + zp or 64 + zp) leaves the
+// exact integer q - zp, and the one multiply by the scale rounds once (to
+// nearest even): the value (q - zp) * s rounded to float16.
+__device__ __forceinline__ h2 dequant_pair_f16(uint32_t w, int h, uint32_t zp, h2 s2, const PairForm &f) {
+    const uint32_t word = h >= 2 ? w >> 8 : w;
+    h2 x, zm;
+    if (h & 1) {
+        x = as_h2((word & f.mask_hi) | f.magic_hi);
+        zm = as_h2(0x54005400u | (zp << 4) | (zp << 20));
+    } else {
+        x = as_h2((word & f.mask_lo) | f.magic_lo);
+        zm = as_h2(0x64006400u | zp | (zp << 16));
+    }
+    return (x - zm) * s2;
 }
+
+// Decode form of pair h: the two codes left in place under a zero exponent,
+// i.e. the exact float16 subnormals q * 2^-24 (h = 0, 2) or q * 2^-20
+// (h = 1, 3, one nibble higher). w8 = w >> 8. A dot product of these with
+// activations is exact up to its float32 accumulation; multiplying the
+// h = 1, 3 sum by 1/16 and then everything by 2^24 restores the codes.
+__device__ __forceinline__ uint32_t subnormal_pair(uint32_t w, uint32_t w8, int h) {
+    const uint32_t v = h >= 2 ? w8 : w;
+    return (h & 1) ? (v & 0x00F000F0u) : (v & 0x000F000Fu);
+}
+constexpr float kSubnormalUnscale = 16777216.0f;  // 2^24
+constexpr float kHighPairScale = 0.0625f;         // 2^-20 -> 2^-24
 
 // Dequantized float32 value: exact integer difference, one float32 multiply.
 __device__ __forceinline__ float dequant_f32(uint32_t code, uint32_t zp, float s) {
     return (float)((int)code - (int)zp) * s;
-}
-
-// Zero point of entry e of a tile's packed zero-point bytes.
-__device__ __forceinline__ uint32_t zp_nibble(const uint8_t *tile_zp, int e) {
-    return (tile_zp[e >> 1] >> (4 * (e & 1))) & 15u;
 }
 
 // float64 -> float16 bits, round half to even, with subnormals, overflow to

@@ -20,8 +20,9 @@
 // group), and each tile's values are read from there. MFMA k-slice t
 // (t = 0..3) uses inputs t*8 .. t*8+7 of the lane's chunk: the lane turns
 // that word into exact (q - zp) float16 pairs with the 1024- and 64-offset
-// tricks and multiplies them by the scale with one rounding (the helper mnb_dequant uses, so the MFMA
-// operands are exactly the dequantized weights). The sum over K does not
+// tricks and multiplies them by the scale with one rounding, in the shared
+// helper dequant_pair_f16 that mnb_dequant also runs, so the MFMA operands
+// are exactly the dequantized weights mnb_dequant returns. The sum over K does not
 // care which inputs an MFMA groups together as long as A and B agree, so A
 // is laid out with the same grouping and no lane shuffles are needed on
 // either side. Two operand slots alternate: slice t is multiplied from one
@@ -29,24 +30,24 @@
 //
 // Instruction order. A stage runs as one fixed sequence (pinned with
 // scheduling barriers): each step issues a fragment's MFMAs, the LDS read of
-// the fragment MNB_GEMM_PIPE steps later into a small register ring, and one
-// or two float16 pairs of the next slice's weights. The compiler's own
-// order, under this kernel's register pressure, left each read one step
-// ahead and waited for every read.
+// the fragment kPipe steps later into a small register ring, and one or two
+// float16 pairs of the next slice's weights. The compiler's own order, under
+// this kernel's register pressure, left each read one step ahead and waited
+// for every read. A wave's issue priority is raised while it runs a stage and
+// lowered at the stage barrier, so that a workgroup in its start or end does
+// not take issue slots from one in its K-loop.
 //
 // Activation side: an LDS stage holds one whole 128-input tile of the
-// workgroup's rows (MNB_GEMM_STAGE_SLICES = 4; 2 splits it in two stages of
-// 64). A stage is a list of 1 KB lines, one per (16-row fragment, slice):
-// byte 16*l of a line holds the 8 inputs lane l passes to that MFMA, so
-// every A read is one conflict-free ds_read_b128 of a contiguous kilobyte.
-// The lines are filled by buffer_load_dwordx4 ... lds, whose 64 lanes write
-// 64 consecutive 16-byte slots: each lane loads the piece its slot needs;
-// the lines of the stage ahead are issued one per step from inside the
-// current stage's MFMA steps.
+// workgroup's rows. A stage is a list of 1 KB lines, one per (16-row
+// fragment, slice): byte 16*l of a line holds the 8 inputs lane l passes to
+// that MFMA, so every A read is one conflict-free ds_read_b128 of a
+// contiguous kilobyte. The lines are filled by buffer_load_dwordx4 ... lds,
+// whose 64 lanes write 64 consecutive 16-byte slots: each lane loads the
+// piece its slot needs; the lines of the stage ahead are issued one per step
+// from inside the current stage's MFMA steps.
 // Rows past M and inputs past K fall outside the buffer's range and read as
 // zero. Two stage buffers (three where they fit) let the loads run one
-// stage (two) ahead, with one barrier per stage; a whole-tile stage halves
-// the barriers of two half-tile stages and measured 7-9% faster.
+// stage (two) ahead, with one barrier per stage.
 //
 // Epilogue: each wave converts its accumulators to float16 into its own LDS
 // area (rows padded by 16 bytes, so the four rows a store instruction
@@ -61,20 +62,7 @@ namespace mnb {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-#ifndef MNB_GEMM_PIPE
-#define MNB_GEMM_PIPE 5  // A-fragment reads kept in flight ahead of the MFMAs that use them
-#endif
-#ifndef MNB_GEMM_PRIO
-// A wave's issue priority is raised while it runs a stage (its MFMAs and
-// the next slice's dequantization) and lowered at the stage barrier, so
-// that a workgroup in its start or end does not take issue slots from one
-// in its K-loop: 0 never, 1 around each step's MFMAs, 2 per stage (1-2%
-// faster at M = 1500 and M = 62; 1 was slower at M = 410).
-#define MNB_GEMM_PRIO 2
-#endif
-#ifndef MNB_GEMM_STAGE_SLICES
-#define MNB_GEMM_STAGE_SLICES 4  // k-slices per LDS stage: 4 (a whole 128-input tile) or 2 (64 inputs)
-#endif
+constexpr int kPipe = 5;  // A-fragment reads kept in flight ahead of the MFMAs that use them
 
 template <int MF, int NF, int WM, int WN, int MaxBufs>
 struct GemmCfg {
@@ -82,8 +70,7 @@ struct GemmCfg {
     static constexpr int kNT = WN * NF * 16;
     static constexpr int kWaves = WM * WN;
     static constexpr int kThreads = 64 * kWaves;
-    static constexpr int kSlices = MNB_GEMM_STAGE_SLICES;  // MFMA k-slices (8 inputs per lane) per stage
-    static constexpr int kStagesPerTile = 4 / kSlices;
+    static constexpr int kSlices = 4;  // MFMA k-slices (8 inputs per lane) per stage: a whole 128-input tile
     static constexpr int kLines = WM * MF * kSlices;  // 1 KB lines per stage
     static constexpr int kLinesPerWave = (kLines + kWaves - 1) / kWaves;
     // every wave issues kLinesPerWave lines; those past kLines load zeros
@@ -96,7 +83,6 @@ struct GemmCfg {
     // as many stage buffers as fit in the CU's 160 KB next to the metadata
     // (at most MaxBufs: 2 or 3)
     static constexpr int kBufs = MaxBufs >= 3 && 3 * kStageBytes + kMetaBytes <= 160 * 1024 ? 3 : 2;
-    static_assert(kSlices == 2 || kSlices == 4, "a stage holds 2 or 4 k-slices");
     // a stage's steps 1, 2, ... issue the lines of the stage ahead, one each
     static_assert(kLinesPerWave < kSlices * MF || kSlices * MF == 1, "a step for every line");
     static constexpr int kMetaOff = kBufs * kStageBytes;
@@ -185,10 +171,8 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     // A line piece starting at input (stage's first) + j * 32 + slice * 8
     // reads zeros when that input is at or past K (only in the last K-tile).
     const int jk = j * kChunk;
-    auto line_dst = [&](int64_t stage) {
-        const int64_t c = stage / C::kStagesPerTile;
-        const int h = (int)(stage % C::kStagesPerTile);
-        const int64_t first = c * kTileK + h * C::kSlices * 8;
+    auto line_dst = [&](int64_t stage) {  // stage = K-tile
+        const int64_t first = stage * kTileK;
         const int64_t left = p.k - first;
         return LineDst{lds + (int)((uint32_t)stage % (uint32_t)C::kBufs) * C::kStageBytes, (uint32_t)(first * 2),
                        (int32_t)(left < kTileK ? left : 0x40000000)};
@@ -259,33 +243,13 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
             R.z[b] = in ? zv : 0u;
         }
     };
-    // B operands of slice t (inputs t*8 .. t*8+7 of the lane's chunk)
-    auto dequant_t = [&](const BRaw<NF> &R, int t, h8 (&out)[NF]) {
-#pragma unroll
-        for (int b = 0; b < NF; ++b) {
-            const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)R.s[b]);
-            const h2 zm = zp_magic(R.zp(b));
-            const h2 s2 = {s, s};
-            const u32x4 w = R.codes[b];
-            const uint32_t word = w[t];
-            h8 v;
-#pragma unroll
-            for (int hh = 0; hh < 4; ++hh) {
-                const h2 d = dequant_pair_f16(word, hh, zm, s2);
-                v[2 * hh] = d.x;
-                v[2 * hh + 1] = d.y;
-            }
-            out[b] = v;
-        }
-    };
-
     f4 acc[MF][NF];
 #pragma unroll
     for (int a = 0; a < MF; ++a)
 #pragma unroll
         for (int b = 0; b < NF; ++b) acc[a][b] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int64_t n_stages = C::kStagesPerTile * p.kg;
+    const int64_t n_stages = p.kg;
     // the next stage's lines must have landed; those two stages ahead may
     // still be in flight (each wave waits for its own loads, then the barrier)
     auto stage_sync = [&](int64_t stage) {
@@ -297,55 +261,46 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
         __syncthreads();
     };
 
-    // Tile c: slices 0..3 in 4 / kSlices stages. Weights of tile c + 1 are
-    // loaded first, so that at each stage end only the newest lines may be
-    // pending. A stage runs in a fixed order: its A fragments (slice by
-    // slice) stream through a ring of MNB_GEMM_PIPE registers, each read
+    // Tile c: slices 0..3 in one stage. Weights of tile c + 1 are loaded
+    // first, so that at the stage end only the newest lines may be pending.
+    // A stage runs in a fixed order: its A fragments (slice by slice)
+    // stream through a ring of kPipe registers, each read
     // issued that many MFMA groups before its use, and each step forms one
     // float16 pair of the next slice's B operands into the free slot (slice t
     // multiplies from slot t & 1).
     h8 s0[NF], s1[NF];
     const int64_t n_groups = (p.kg + kMetaGroup - 1) / kMetaGroup;
-    // Pairs hh = 0 and 2 (nibbles at bits 0 and 16, after a shift by 8 for
-    // hh = 2) become 1024 + q under the 0x6400 exponent, whose ulp is 1;
-    // pairs hh = 1 and 3 sit 4 bits higher and become 64 + q under 0x5400,
-    // whose ulp is 1/16, with no shift. Subtracting 1024 + zp or 64 + zp
-    // leaves the same exact q - zp, times the scale with one rounding (the
-    // value dequant_pair_f16 forms). The masks and offsets are held in
-    // registers (literal constants cannot go into the three-operand form),
-    // so that masking a pair and adding the offset is one v_and_or_b32.
-    uint32_t pair_mask = 0x000F000Fu, pair_mask_hi = 0x00F000F0u, pair_magic = 0x64006400u, pair_magic_hi = 0x54005400u;
+    // B operands: float16 pairs in the shared dequant pair form, whose masks
+    // and offsets are held in registers (literal constants cannot go into
+    // the three-operand form), so that masking a pair and adding the offset
+    // is one v_and_or_b32.
+    PairForm pf = pair_form_literal();
 #if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(pair_mask));
-    asm volatile("s_mov_b32 %0, 0x00f000f0" : "=s"(pair_mask_hi));
-    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(pair_magic));
-    asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(pair_magic_hi));
+    asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(pf.mask_lo));
+    asm volatile("s_mov_b32 %0, 0x00f000f0" : "=s"(pf.mask_hi));
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(pf.magic_lo));
+    asm volatile("v_mov_b32 %0, 0x54005400" : "=v"(pf.magic_hi));
 #endif
     auto put_pair = [&](const BRaw<NF> &R, int t, int b, int hh, h8 &dst) {
         const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)R.s[b]);
-        const uint32_t zp = R.zp(b);
         const h2 s2 = {s, s};
-        const u32x4 w = R.codes[b];
-        const uint32_t word = hh >= 2 ? w[t] >> 8 : w[t];
-        h2 x, zm;
-        if (hh & 1) {
-            x = as_h2((word & pair_mask_hi) | pair_magic_hi);
-            zm = as_h2(0x54005400u | (zp << 4) | (zp << 20));
-        } else {
-            x = as_h2((word & pair_mask) | pair_magic);
-            zm = zp_magic(zp);
-        }
-        const h2 d = (x - zm) * s2;
+        const h2 d = dequant_pair_f16(R.codes[b][t], hh, R.zp(b), s2, pf);
         dst[2 * hh] = d.x;
         dst[2 * hh + 1] = d.y;
     };
-    // Stage `stage` (stage h of its tile: slices h*kSlices .. + kSlices - 1):
-    // each step forms one pair of the next slice's B operands, from Rc, or
-    // from Rn (the next tile's slice 0) after the tile's last slice.
-    auto run_stage = [&](int64_t stage, auto h_tag, const BRaw<NF> &Rc, const BRaw<NF> &Rn, auto &&step_hook) {
-        constexpr int h = decltype(h_tag)::value;
+    // B operands of slice t (inputs t*8 .. t*8+7 of the lane's chunk)
+    auto dequant_t = [&](const BRaw<NF> &R, int t, h8 (&out)[NF]) {
+#pragma unroll
+        for (int b = 0; b < NF; ++b)
+#pragma unroll
+            for (int hh = 0; hh < 4; ++hh) put_pair(R, t, b, hh, out[b]);
+    };
+    // Stage `stage` (K-tile `stage`, slices 0..3): each step forms one pair
+    // of the next slice's B operands, from Rc, or from Rn (the next tile's
+    // slice 0) after the tile's last slice.
+    auto run_stage = [&](int64_t stage, const BRaw<NF> &Rc, const BRaw<NF> &Rn, auto &&step_hook) {
         constexpr int S = C::kSlices;
-        constexpr int R = MNB_GEMM_PIPE < S * MF ? MNB_GEMM_PIPE : S * MF;
+        constexpr int R = kPipe < S * MF ? kPipe : S * MF;
         constexpr int kPieces = NF * 4;
         const uint8_t *base = lds + (int)((uint32_t)stage % (uint32_t)C::kBufs) * C::kStageBytes +
                               (wm * MF * S) * 1024 + lane * 16;
@@ -356,24 +311,16 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
             else put_pair(Rn, 0, k / 4, k % 4, dst);
         };
         h8 ring[R];
-#if MNB_GEMM_PRIO == 2
         __builtin_amdgcn_s_setprio(1);
-#endif
 #pragma unroll
         for (int i = 0; i < R; ++i) ring[i] = frag(i);
 #pragma unroll
         for (int q = 0; q < S * MF; ++q) {
-            const int tt = q / MF, a = q % MF, t = h * S + tt;
+            const int t = q / MF, a = q % MF;
             const h8 av = ring[q % R];
-#if MNB_GEMM_PRIO == 1
-            __builtin_amdgcn_s_setprio(1);
-#endif
 #pragma unroll
             for (int b = 0; b < NF; ++b)
                 acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, (t & 1) ? s1[b] : s0[b], acc[a][b], 0, 0, 0);
-#if MNB_GEMM_PRIO == 1
-            __builtin_amdgcn_s_setprio(0);
-#endif
             if (q + R < S * MF) ring[q % R] = frag(q + R);
             step_hook(q);
             // pairs per step: 2 for the small-M tiles (16 pairs per slice
@@ -388,9 +335,7 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-#if MNB_GEMM_PRIO == 2
         __builtin_amdgcn_s_setprio(0);
-#endif
     };
     // Each stage's steps 1, 2, ... issue one activation line each of the
     // stage ahead, where the MFMAs around them cover their issue. Every wave
@@ -400,24 +345,17 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     // never falls back to waiting for all of them.
     // (after the last K-tile Rn holds no weights; its slice is formed and never used)
     auto tile = [&](int64_t c, const BRaw<NF> &Rc, BRaw<NF> &Rn) {
-        const int64_t st = C::kStagesPerTile * c;
+        const int64_t st = c;
         if (c % kMetaGroup == 0 && c / kMetaGroup + 1 < n_groups) issue_meta(c / kMetaGroup + 1);
         if (c + 1 < p.kg) {
             load_codes(c + 1, Rn);
             read_meta(c + 1, Rn);
         }
         const LineDst d = line_dst(st + (C::kBufs == 3 ? 2 : 1));
-        run_stage(st, std::integral_constant<int, 0>{}, Rc, Rn, [&](int q) {
+        run_stage(st, Rc, Rn, [&](int q) {
             if (q >= 1 && q <= C::kLinesPerWave) issue_line(d, q - 1);
         });
         stage_sync(st);
-        if constexpr (C::kStagesPerTile == 2) {
-            const LineDst d1 = line_dst(st + (C::kBufs == 3 ? 3 : 2));
-            run_stage(st + 1, std::integral_constant<int, 1>{}, Rc, Rn, [&](int q) {
-                if (q >= 1 && q <= C::kLinesPerWave) issue_line(d1, q - 1);
-            });
-            stage_sync(st + 1);
-        }
     };
 
     BRaw<NF> R0, R1;
@@ -546,39 +484,19 @@ __global__ __launch_bounds__(64 * WM *WN) void gemm_grouped_kernel(const Problem
 // ---------------------------------------------------------------------------
 // Variants and their selection.
 // ---------------------------------------------------------------------------
-// 16-row fragments (NF) per wave of the small-M tiles
-#ifndef MNB_GEMM_NF0
-#define MNB_GEMM_NF0 4
-#endif
-#ifndef MNB_GEMM_NF1
-#define MNB_GEMM_NF1 4
-#endif
-#ifndef MNB_GEMM_NF2
-#define MNB_GEMM_NF2 4
-#endif
-// stage buffers at most, per tile shape
-#ifndef MNB_GEMM_BUFS_SMALL
-#define MNB_GEMM_BUFS_SMALL 3
-#endif
-#ifndef MNB_GEMM_BUFS_MID
-#define MNB_GEMM_BUFS_MID 2
-#endif
 struct VariantInfo {
     int mt, nt;
 };
 static const VariantInfo kVariants[] = {
-    {16, 64 * MNB_GEMM_NF0},  // 0: MF 1,  1x4 waves
-    {32, 64 * MNB_GEMM_NF1},  // 1: MF 2,  1x4 waves
-    {64, 64 * MNB_GEMM_NF2},  // 2: MF 4,  1x4 waves
+    {16, 256},                // 0: MF 1,  NF 4, 1x4 waves
+    {32, 256},                // 1: MF 2,  NF 4, 1x4 waves
+    {64, 256},                // 2: MF 4,  NF 4, 1x4 waves
     {208, 256},               // 3: MF 13, NF 2, 1x8 waves
     {192, 256},               // 4: MF 12, NF 2, 1x8 waves
 };
 constexpr int kNumVariants = 5;
 
 int gemm_variant(int64_t m) {
-#ifdef MNB_GEMM_FORCE_VARIANT
-    if (m > 64) return MNB_GEMM_FORCE_VARIANT;
-#endif
     if (m <= 16) return 0;
     if (m <= 32) return 1;
     if (m <= 64) return 2;
@@ -604,10 +522,10 @@ void gemm_tiles(const Problem &p, int variant, int32_t *tiles_m, int32_t *tiles_
 }
 
 // (variant, MF, NF, WM, WN, stage buffers at most)
-#define MNB_GEMM_VARIANTS(X)                          \
-    X(0, 1, MNB_GEMM_NF0, 1, 4, MNB_GEMM_BUFS_SMALL)  \
-    X(1, 2, MNB_GEMM_NF1, 1, 4, MNB_GEMM_BUFS_SMALL)  \
-    X(2, 4, MNB_GEMM_NF2, 1, 4, MNB_GEMM_BUFS_MID)    \
+#define MNB_GEMM_VARIANTS(X) \
+    X(0, 1, 4, 1, 4, 3)      \
+    X(1, 2, 4, 1, 4, 3)      \
+    X(2, 4, 4, 1, 4, 2)      \
     X(3, 13, 2, 1, 8, 3)                              \
     X(4, 12, 2, 1, 8, 3)
 

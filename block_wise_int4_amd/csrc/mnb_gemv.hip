@@ -25,6 +25,8 @@
 // - zp * sum_k x_k, with the chunk sum of x read from LDS, and the block
 // scale multiplies the chunk result once. The four chunk lanes of each row
 // are summed with two cross-lane exchanges at the end of the row group.
+#include <atomic>
+
 #include "../../include/mnb.h"
 #include "mnb_internal.h"
 
@@ -32,38 +34,24 @@ namespace mnb {
 
 constexpr int kGemvWaves = 4;
 constexpr int kGemvThreads = 64 * kGemvWaves;
-#ifndef MNB_DECODE_TG
-#define MNB_DECODE_TG 8
-#endif
-constexpr int kTG = MNB_DECODE_TG;  // tiles per load group (4 or 8; divides the metadata group)
-static_assert(kMetaGroup % kTG == 0, "load groups must not straddle metadata groups");
-
-#ifndef MNB_DECODE_TWO_MASK
-#define MNB_DECODE_TWO_MASK 1
-#endif
-#ifndef MNB_DECODE_NT
-#define MNB_DECODE_NT 1
-#endif
+constexpr int kTG = 8;  // tiles per load group: one metadata group
+static_assert(kMetaGroup == kTG, "a load group is one metadata group");
+constexpr int kDecodeOcc = 3;  // decode workgroups per CU (12 waves)
 
 // Scales of TG consecutive tiles, read with one vector load.
 template <typename T, int TG>
 struct ScaleVec {
     static constexpr int kWords = TG * (int)sizeof(T) / 4;
     uint32_t w[kWords];
+    static_assert(kWords % 4 == 0, "whole 16-byte loads");
     __device__ void load(const uint8_t *p) {
-        if constexpr (kWords == 2) {
-            const uint2 v = *reinterpret_cast<const uint2 *>(p);
-            w[0] = v.x;
-            w[1] = v.y;
-        } else {
 #pragma unroll
-            for (int i = 0; i < kWords / 4; ++i) {
-                const u32x4 v = reinterpret_cast<const u32x4 *>(p)[i];
-                w[4 * i + 0] = v.x;
-                w[4 * i + 1] = v.y;
-                w[4 * i + 2] = v.z;
-                w[4 * i + 3] = v.w;
-            }
+        for (int i = 0; i < kWords / 4; ++i) {
+            const u32x4 v = reinterpret_cast<const u32x4 *>(p)[i];
+            w[4 * i + 0] = v.x;
+            w[4 * i + 1] = v.y;
+            w[4 * i + 2] = v.z;
+            w[4 * i + 3] = v.w;
         }
     }
     __device__ float get(int u) const {
@@ -92,16 +80,11 @@ __device__ __forceinline__ void load_group(const Problem &p, int64_t g, int64_t 
     const int64_t nt = p.kg - c0;
 #pragma unroll
     for (int u = 0; u < kTG; ++u) {
-#if MNB_DECODE_NT
         if (u < nt) G.codes[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + u * kTileCodeBytes));
-#else
-        if (u < nt) G.codes[u] = *reinterpret_cast<const u32x4 *>(base + u * kTileCodeBytes);
-#endif
         else G.codes[u] = u32x4{0u, 0u, 0u, 0u};
     }
     G.s.load(p.packed + p.scales_off + mi * (int64_t)sizeof(T));
-    if constexpr (kTG == 8) G.z = *reinterpret_cast<const uint32_t *>(p.packed + p.zp_off + (mi >> 1));
-    else G.z = *reinterpret_cast<const uint16_t *>(p.packed + p.zp_off + (mi >> 1));
+    G.z = *reinterpret_cast<const uint32_t *>(p.packed + p.zp_off + (mi >> 1));
 }
 
 // Contribution of tiles [c0, c0 + kTG) to the lane's partial dot product.
@@ -121,31 +104,21 @@ __device__ __forceinline__ float group_math(const Group<T> &G, int64_t nt, const
         float part = 0.0f;
         if constexpr (sizeof(T) == 2) {
             const u32x4 *xv = reinterpret_cast<const u32x4 *>(xg + u * kTileK);
-#if MNB_DECODE_TWO_MASK
-            // pairs 0 and 2 masked in place (q * 2^-24), pairs 1 and 3 masked
-            // one nibble higher (q * 2^-20) into a second sum scaled back by
-            // 1/16 at the end: one shift per word instead of three
+            // pairs 0 and 2 in place (q * 2^-24), pairs 1 and 3 one nibble
+            // higher (q * 2^-20) into a second sum scaled back at the end: one
+            // shift per word instead of three
             float part_hi = 0.0f;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const u32x4 xx = xv[t];
                 const uint32_t w0 = w[t], w8 = w[t] >> 8;
-                part = __builtin_amdgcn_fdot2(as_h2(w0 & 0x000F000Fu), as_h2(xx[0]), part, false);
-                part_hi = __builtin_amdgcn_fdot2(as_h2(w0 & 0x00F000F0u), as_h2(xx[1]), part_hi, false);
-                part = __builtin_amdgcn_fdot2(as_h2(w8 & 0x000F000Fu), as_h2(xx[2]), part, false);
-                part_hi = __builtin_amdgcn_fdot2(as_h2(w8 & 0x00F000F0u), as_h2(xx[3]), part_hi, false);
+                part = __builtin_amdgcn_fdot2(as_h2(subnormal_pair(w0, w8, 0)), as_h2(xx[0]), part, false);
+                part_hi = __builtin_amdgcn_fdot2(as_h2(subnormal_pair(w0, w8, 1)), as_h2(xx[1]), part_hi, false);
+                part = __builtin_amdgcn_fdot2(as_h2(subnormal_pair(w0, w8, 2)), as_h2(xx[2]), part, false);
+                part_hi = __builtin_amdgcn_fdot2(as_h2(subnormal_pair(w0, w8, 3)), as_h2(xx[3]), part_hi, false);
             }
-            part = __builtin_fmaf(part_hi, 0.0625f, part);
-#else
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const u32x4 xx = xv[t];
-#pragma unroll
-                for (int h = 0; h < 4; ++h)
-                    part = __builtin_amdgcn_fdot2(as_h2((w[t] >> (4 * h)) & 0x000F000Fu), as_h2(xx[h]), part, false);
-            }
-#endif
-            part = __builtin_fmaf(part, 16777216.0f, -zs);  // 2^24 undoes the subnormal scaling exactly
+            part = __builtin_fmaf(part_hi, kHighPairScale, part);
+            part = __builtin_fmaf(part, kSubnormalUnscale, -zs);  // 2^24 undoes the subnormal scaling exactly
         } else {
             const float4 *xv = reinterpret_cast<const float4 *>(xg + u * kTileK);
 #pragma unroll
@@ -272,12 +245,8 @@ __device__ __forceinline__ uint64_t decode_range(const Problem *entries, Problem
     return best;
 }
 
-#ifndef MNB_DECODE_OCC
-#define MNB_DECODE_OCC 3
-#endif
-
 template <typename T>
-__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(MNB_DECODE_OCC)))
+__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(kDecodeOcc)))
 void decode_kernel(Problem p, int64_t wgs) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int64_t nbat = p.batch_end;  // batch_begin = 0 for a single problem
@@ -291,7 +260,7 @@ static_assert(kGemvMaxWgs * 8 <= MNB_ARGMAX_WORKSPACE_BYTES, "argmax workspace t
 // Decode product fused with a greedy argmax over its outputs: each
 // workgroup stores the best key of the outputs it produced in its slot.
 template <typename T>
-__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(MNB_DECODE_OCC)))
+__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(kDecodeOcc)))
 void decode_argmax_kernel(Problem p, int64_t wgs, unsigned long long *slots) {
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ unsigned long long wave_best[kGemvWaves];
@@ -337,7 +306,7 @@ __global__ __launch_bounds__(kGemvThreads) void argmax_finish_kernel(const unsig
 }
 
 template <typename T>
-__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(MNB_DECODE_OCC)))
+__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(kDecodeOcc)))
 void decode_grouped_kernel(const Problem *entries, const GemvWg *table) {
     extern __shared__ __align__(16) uint8_t smem[];
     const GemvWg w = table[blockIdx.x];
@@ -464,12 +433,23 @@ int64_t gemv_workgroups(const Problem &p, int variant) {
     return ((p.rg + kGemvWaves - 1) / kGemvWaves) * ((p.m + mr - 1) / mr);
 }
 
-// Kernels whose dynamic LDS exceeds the default must say so once per size.
-template <typename K>
-static hipError_t allow_lds(K kernel, size_t lds) {
+// Kernels whose dynamic LDS may exceed the default must opt in. Each kernel's
+// limit is raised once per device, to the largest size any call can ask
+// for, and never lowered, so concurrent callers cannot undo each other's
+// setting and later calls skip the runtime call.
+template <auto Kernel>
+static hipError_t allow_lds(size_t lds) {
     if (lds <= (size_t)kDefaultLds) return hipSuccess;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)lds);
+    static std::atomic<uint64_t> raised{0};  // bit d: raised on device d (devices 0..63)
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = dev >= 0 && dev < 64 ? 1ull << dev : 0ull;
+    if (bit && (raised.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            kGemvMaxLds);
+    if (e == hipSuccess && bit) raised.fetch_or(bit, std::memory_order_release);
+    return e;
 }
 
 int64_t gemv_schedule(Problem *entries, int count, GemvWg *table, int max_wgs) {
@@ -512,10 +492,10 @@ hipError_t launch_gemv(const Problem &p0, int dtype, int variant, hipStream_t st
     if (variant >= 2) {
         const unsigned grid = (unsigned)gemv_workgroups(p0, variant);
         if (variant == 2) {
-            if ((e = allow_lds(rows_kernel<kRowsMR>, lds)) != hipSuccess) return e;
+            if ((e = allow_lds<rows_kernel<kRowsMR>>(lds)) != hipSuccess) return e;
             rows_kernel<kRowsMR><<<grid, kGemvThreads, lds, st>>>(p0);
         } else {
-            if ((e = allow_lds(rows_kernel<1>, lds)) != hipSuccess) return e;
+            if ((e = allow_lds<rows_kernel<1>>(lds)) != hipSuccess) return e;
             rows_kernel<1><<<grid, kGemvThreads, lds, st>>>(p0);
         }
         return hipGetLastError();
@@ -525,10 +505,10 @@ hipError_t launch_gemv(const Problem &p0, int dtype, int variant, hipStream_t st
     p.batch_end = (p.rg + kGemvWaves - 1) / kGemvWaves;
     const int64_t wgs = p.batch_end < kGemvMaxWgs ? p.batch_end : kGemvMaxWgs;
     if (variant == 0) {
-        if ((e = allow_lds(decode_kernel<_Float16>, lds)) != hipSuccess) return e;
+        if ((e = allow_lds<decode_kernel<_Float16>>(lds)) != hipSuccess) return e;
         decode_kernel<_Float16><<<(unsigned)wgs, kGemvThreads, lds, st>>>(p, wgs);
     } else {
-        if ((e = allow_lds(decode_kernel<float>, lds)) != hipSuccess) return e;
+        if ((e = allow_lds<decode_kernel<float>>(lds)) != hipSuccess) return e;
         decode_kernel<float><<<(unsigned)wgs, kGemvThreads, lds, st>>>(p, wgs);
     }
     return hipGetLastError();
@@ -543,10 +523,10 @@ hipError_t launch_gemv_argmax(const Problem &p0, int variant, void *workspace, i
     unsigned long long *slots = static_cast<unsigned long long *>(workspace);
     hipError_t e = hipSuccess;
     if (variant == 0) {
-        if ((e = allow_lds(decode_argmax_kernel<_Float16>, lds)) != hipSuccess) return e;
+        if ((e = allow_lds<decode_argmax_kernel<_Float16>>(lds)) != hipSuccess) return e;
         decode_argmax_kernel<_Float16><<<(unsigned)wgs, kGemvThreads, lds, st>>>(p, wgs, slots);
     } else if (variant == 1) {
-        if ((e = allow_lds(decode_argmax_kernel<float>, lds)) != hipSuccess) return e;
+        if ((e = allow_lds<decode_argmax_kernel<float>>(lds)) != hipSuccess) return e;
         decode_argmax_kernel<float><<<(unsigned)wgs, kGemvThreads, lds, st>>>(p, wgs, slots);
     } else {
         return hipErrorInvalidValue;
@@ -561,19 +541,19 @@ hipError_t launch_gemv_grouped(const Problem *dev_entries, int count, const Gemv
     hipError_t e = hipSuccess;
     switch (variant) {
     case 0:
-        if ((e = allow_lds(decode_grouped_kernel<_Float16>, lds)) != hipSuccess) return e;
+        if ((e = allow_lds<decode_grouped_kernel<_Float16>>(lds)) != hipSuccess) return e;
         decode_grouped_kernel<_Float16><<<(unsigned)wgs, kGemvThreads, lds, st>>>(dev_entries, dev_table);
         break;
     case 1:
-        if ((e = allow_lds(decode_grouped_kernel<float>, lds)) != hipSuccess) return e;
+        if ((e = allow_lds<decode_grouped_kernel<float>>(lds)) != hipSuccess) return e;
         decode_grouped_kernel<float><<<(unsigned)wgs, kGemvThreads, lds, st>>>(dev_entries, dev_table);
         break;
     case 2:
-        if ((e = allow_lds(rows_grouped_kernel<kRowsMR>, lds)) != hipSuccess) return e;
+        if ((e = allow_lds<rows_grouped_kernel<kRowsMR>>(lds)) != hipSuccess) return e;
         rows_grouped_kernel<kRowsMR><<<(unsigned)wgs, kGemvThreads, lds, st>>>(dev_entries, count);
         break;
     default:
-        if ((e = allow_lds(rows_grouped_kernel<1>, lds)) != hipSuccess) return e;
+        if ((e = allow_lds<rows_grouped_kernel<1>>(lds)) != hipSuccess) return e;
         rows_grouped_kernel<1><<<(unsigned)wgs, kGemvThreads, lds, st>>>(dev_entries, count);
         break;
     }

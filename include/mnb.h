@@ -20,8 +20,9 @@
  *  - Pointers named x, y, w, qweight, scales, zero_points, packed, q, zp are
  *    DEVICE pointers. The caller owns all memory; the library allocates,
  *    frees and synchronizes nothing and keeps no state between calls (beyond
- *    raising a kernel's LDS limit the first time a long K needs it), so calls
- *    are reentrant. Calls on one stream run in order.
+ *    raising a kernel's LDS limit, once per device and to its maximum, the
+ *    first time a long K needs it), so calls are reentrant. Calls on one
+ *    stream run in order.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Every call that touches device memory is asynchronous on it.
  *  - bits must be 4, block_size 32, 64, 128 or 256, K a positive multiple of
@@ -123,6 +124,12 @@ int mnb_quantize_rtn(const float *w, int64_t N, int64_t K, int bits, int block_s
 /*
  * Canonical format -> the device layout the compute kernels read, written to
  * `packed` (mnb_packed_bytes(...) bytes, device). Runs once per weight.
+ * The canonical format is the one the conversion writes: 4-bit codes in
+ * blocks of block_size along K with one scale and one 4-bit zero point per
+ * block ("Mega-ASR INT4 ONNX", section "Conversion details"), low nibble
+ * first. Inputs: qweight [N][K/2], scales [N][K/bs] of dtype, zero_points
+ * [N][ceil(K/bs/2)], all device, all read only; the device layout is
+ * described with the library's sources and is not an interface.
  * zero_points NULL: the symmetric format, stored as zero point 8 for every
  * block (the compute kernels then run unchanged).
  */
@@ -132,23 +139,35 @@ int mnb_pack(const uint8_t *qweight, const void *scales, const uint8_t *zero_poi
 
 /*
  * Test export: the unpacked codes q uint8 [N][K] (values 0..15) and zero
- * points zp uint8 [N][K/bs], read back from `packed` with the same device
- * functions the compute kernels use. Bit-exact with the canonical input.
+ * points zp uint8 [N][K/bs] of the format in "Mega-ASR INT4 ONNX", section
+ * "Conversion details", read back from `packed` (device, read only) into
+ * device buffers the caller owns. Each code is read through the pair form
+ * the float16 decode kernel feeds its dot products (the codes as exact
+ * float16 subnormals), and must agree with the reader the float32 kernels
+ * use; a code where the two disagree reads 0xFF. Bit-exact with the
+ * canonical input.
  */
 int mnb_unpack(const void *packed, int64_t N, int64_t K, int bits, int block_size, int dtype,
                uint8_t *q, uint8_t *zp, void *stream);
 
 /*
- * Test export: dequantized weights w [N][K] in dtype, each (q - zp) formed
- * exactly and multiplied by s with one round-half-to-even rounding, using
- * the same device functions as the GEMM's weight tiles. Bit-exact.
+ * Test export: dequantized weights w [N][K] in dtype (device, caller-owned),
+ * D = (q - zp) * s per block ("Mega-ASR INT4 ONNX", section "Conversion
+ * details": asymmetric codes with a zero point), each (q - zp) formed
+ * exactly and multiplied by s with one round-half-to-even rounding. Float16
+ * weights come from the same pair helper that forms the matrix-core
+ * kernel's operands, so they are bitwise the values that kernel multiplies.
+ * Bit-exact.
  */
 int mnb_dequant(const void *packed, int64_t N, int64_t K, int bits, int block_size, int dtype,
                 void *w, void *stream);
 
 /*
- * Decode-step product, M = 1: y[N] = x[K] * D^T. x and y are dtype.
- * Accumulates in float32 and rounds y once to dtype.
+ * Decode-step product, M = 1: y[N] = x[K] * D^T, the step graph's one new
+ * position ("Qwen3-ASR-0.6B ONNX for the browser", section "Graph
+ * contracts"). x [K] and y [N] are device buffers of dtype; packed is the
+ * mnb_pack output for (N, K, block_size, dtype). Accumulates in float32 and
+ * rounds y once to dtype.
  */
 int mnb_gemv(const void *x, const void *packed, void *y,
              int64_t N, int64_t K, int bits, int block_size, int dtype, void *stream);
@@ -190,10 +209,12 @@ int mnb_embed_gather(const int8_t *table, const float *row_scales, const int64_t
 
 /*
  * General product for any M >= 1: Y[M][N] = X[M][K] * D^T, X and Y
- * row-major in dtype. M = 1 runs the decode kernel; float16 with M >= 2
- * runs the matrix-core (MFMA) kernel that dequantizes weight tiles and feeds
- * fp16 MFMA with float32 accumulation; float32 with M >= 2 runs a vector
- * kernel.
+ * row-major device buffers in dtype; only the weights are quantized and the
+ * activations enter as they are ("sherpa-onnx STT int4", section "Why int4
+ * rather than the usual int8"). M = 1 runs the decode kernel; float16 with
+ * M >= 2 runs the matrix-core (MFMA) kernel that dequantizes weight tiles
+ * and feeds fp16 MFMA with float32 accumulation; float32 with M >= 2 runs a
+ * vector kernel.
  */
 int mnb_gemm(const void *x, const void *packed, void *y,
              int64_t M, int64_t N, int64_t K, int bits, int block_size, int dtype, void *stream);
