@@ -158,6 +158,22 @@ int mnb_gemv_argmax(const void *x, const void *packed, void *y, int64_t *index, 
     return hip_status(launch_gemv_argmax(p, variant, workspace, index, as_stream(stream)));
 }
 
+int mnb_gemv_argmax_noalloc(const void *x, const void *packed, void *y, int64_t *index, int64_t N, int64_t K,
+                            int bits, int block_size, int dtype, void *stream) {
+    if (!index) return MNB_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(index) & 7) return MNB_ERR_ALIGN;
+    Problem p;
+    int kind = 0, variant = 0;
+    int st = prepare_product(x, packed, y ? y : x, 1, N, K, bits, block_size, dtype, &p, &kind, &variant);
+    if (st) return st;
+    p.y = y;
+    void *slots = nullptr;
+    int64_t n_slots = 0;
+    if (argmax_scratch(&slots, &n_slots) != hipSuccess) return MNB_ERR_HIP;
+    if (gemv_argmax_slots(p) > n_slots) return MNB_ERR_SHAPE;
+    return hip_status(launch_gemv_argmax(p, variant, slots, index, as_stream(stream)));
+}
+
 int mnb_gemv(const void *x, const void *packed, void *y, int64_t N, int64_t K, int bits, int block_size, int dtype,
              void *stream) {
     return mnb_gemm(x, packed, y, 1, N, K, bits, block_size, dtype, stream);

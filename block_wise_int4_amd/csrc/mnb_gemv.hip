@@ -26,6 +26,7 @@
 // scale multiplies the chunk result once. The four chunk lanes of each row
 // are summed with two cross-lane exchanges at the end of the row group.
 #include <atomic>
+#include <mutex>
 
 #include "../../include/mnb.h"
 #include "mnb_internal.h"
@@ -534,6 +535,47 @@ hipError_t launch_gemv_argmax(const Problem &p0, int variant, void *workspace, i
     if ((e = hipGetLastError()) != hipSuccess) return e;
     argmax_finish_kernel<<<1, kGemvThreads, 0, st>>>(slots, (int)wgs, index);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Library-held argmax slots for callers that cannot allocate: one array per
+// device (the runtime gives each device its own copy), holding one slot per
+// workgroup of the largest argmax launch. Host code never passes the
+// array's name to a kernel: in host code it is a stand-in, not a device
+// address. Its address on each device comes from hipGetSymbolAddress, once
+// per device, with that device current.
+// ---------------------------------------------------------------------------
+constexpr int kScratchSlots = kGemvMaxWgs;
+static __device__ __align__(256) unsigned long long scratch[kScratchSlots];
+
+constexpr int kMaxScratchDevices = 64;
+static std::atomic<void *> g_scratch_ptr[kMaxScratchDevices];
+static std::mutex g_scratch_mu;
+
+hipError_t argmax_scratch(void **slots, int64_t *n_slots) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    void *ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+        if (!ptr) {
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!ptr) return hipErrorInvalidSymbol;
+            g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *slots = ptr;
+    *n_slots = kScratchSlots;
+    return hipSuccess;
+}
+
+int64_t gemv_argmax_slots(const Problem &p) {
+    const int64_t batches = (p.rg + kGemvWaves - 1) / kGemvWaves;
+    return batches < kGemvMaxWgs ? batches : kGemvMaxWgs;
 }
 
 hipError_t launch_gemv_grouped(const Problem *dev_entries, int count, const GemvWg *dev_table, int64_t wgs,

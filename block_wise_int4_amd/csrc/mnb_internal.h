@@ -119,6 +119,11 @@ hipError_t launch_embed_gather(const int8_t *table, const float *scales, const i
                                int64_t vocab, int64_t h, int dtype, void *out, hipStream_t st);
 // Decode product (variants 0 and 1) fused with a greedy argmax of y.
 hipError_t launch_gemv_argmax(const Problem &p, int variant, void *workspace, int64_t *index, hipStream_t st);
+// Workspace slots the argmax launch of p writes (one per workgroup).
+int64_t gemv_argmax_slots(const Problem &p);
+// This device's library-held argmax slots (device address and slot count),
+// looked up once per device.
+hipError_t argmax_scratch(void **slots, int64_t *n_slots);
 hipError_t launch_gemv_grouped(const Problem *dev_entries, int count, const GemvWg *dev_table, int64_t wgs,
                                int variant, size_t lds, hipStream_t st);
 

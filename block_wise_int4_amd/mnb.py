@@ -53,6 +53,7 @@ _SIGNATURES = {
     "mnb_dequant": (_int, [_vp, _i64, _i64, _int, _int, _int, _vp, _vp]),
     "mnb_gemv": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
     "mnb_gemv_argmax": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
+    "mnb_gemv_argmax_noalloc": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
     "mnb_embed_gather": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _vp]),
     "mnb_gemm": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp]),
     "mnb_plan_bytes": (_sz, [_int]),
@@ -269,6 +270,26 @@ def mnb_gemv_argmax(x, pw, workspace, y=None, index=None, logits=False):
         _dev(x, "x"), _dev(pw.packed, "packed"), None if y is None else _dev(y, "y"), _dev(index, "index"),
         _dev(workspace, "workspace"), pw.N, pw.K, pw.bits, pw.block_size, dtype_code(pw.dtype),
         _stream(x.device)))
+    return (index, y) if y is not None else index
+
+
+def mnb_gemv_argmax_noalloc(x, pw, y=None, index=None, logits=False):
+    """mnb_gemv_argmax with the library's own per-device partial-result
+    slots instead of a workspace (for callers that cannot allocate); calls
+    that may overlap on one device race."""
+    _check_x(x, pw)
+    if x.numel() != pw.K:
+        raise ValueError("mnb_gemv_argmax_noalloc takes one activation row")
+    if y is None and logits:
+        y = torch.empty(pw.N, dtype=pw.dtype, device=x.device)
+    if y is not None:
+        _check_buf(y, "y", pw.dtype, pw.N, x.device)
+    if index is None:
+        index = torch.empty(1, dtype=torch.int64, device=x.device)
+    _check_buf(index, "index", torch.int64, 1, x.device)
+    _check("mnb_gemv_argmax_noalloc", lib().mnb_gemv_argmax_noalloc(
+        _dev(x, "x"), _dev(pw.packed, "packed"), None if y is None else _dev(y, "y"), _dev(index, "index"),
+        pw.N, pw.K, pw.bits, pw.block_size, dtype_code(pw.dtype), _stream(x.device)))
     return (index, y) if y is not None else index
 
 

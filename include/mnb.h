@@ -193,6 +193,25 @@ int mnb_gemv_argmax(const void *x, const void *packed, void *y, int64_t *index, 
                     int64_t N, int64_t K, int bits, int block_size, int dtype, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc): the same
+ * product and argmax as mnb_gemv_argmax, with the per-workgroup partial
+ * results kept in a device array the library holds instead of a caller
+ * workspace. The array holds 768 slots (6 KB) per device, the most any
+ * argmax launch uses, so no N or K within the documented limits is
+ * rejected for its sake; a launch that would need more slots returns
+ * MNB_ERR_SHAPE. The array is looked up once per device, on the first call
+ * on that device; nothing is allocated or freed, and each device keeps its
+ * copy until the process ends. Every call on a device shares that device's
+ * array: calls that may overlap on one device (different streams) race and
+ * must not be issued; calls one after another on one stream are safe. The
+ * array needs no clearing: each call writes every slot it reads. Arguments,
+ * results and errors otherwise as mnb_gemv_argmax.
+ */
+int mnb_gemv_argmax_noalloc(const void *x, const void *packed, void *y, int64_t *index,
+                            int64_t N, int64_t K, int bits, int block_size, int dtype, void *stream);
+
+/*
  * The step before the product in decode: the next input embeddings, as
  * int8 rows of the token table times each row's float32 scale ("Qwen3-ASR-
  * 0.6B ONNX for the browser", section "Building the prompt": an int8 row
