@@ -114,6 +114,84 @@ def record_traffic(fetch_csv, write_csv, probe_mib, workloads, command):
     print("\n".join(lines))
 
 
+def summarize_trace(trace_csv, bench_json, command, out_dir):
+    """Kernel-trace summaries for profiles/: from a rocprofv3 --kernel-trace
+    CSV of a bench.py run and that run's JSON line, one markdown file per
+    timed workload (named kernel__workload), giving the trace's average
+    duration over the timed launches beside bench.py's own HIP-event figure.
+
+    A workload's grouped launches (first launch, warm-up, timed steps) run
+    back to back, so they are the workload's run of consecutive dispatches
+    of its kernel; runs of one kernel are matched to workloads in the order
+    bench.py times them."""
+    import csv
+    import re
+
+    rows = list(csv.DictReader(open(trace_csv)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    runs = []  # (kernel name, [durations in us])
+    for r in rows:
+        name = r["Kernel_Name"]
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if runs and runs[-1][0] == name:
+            runs[-1][1].append(d)
+        else:
+            runs.append((name, [d]))
+    line = [ln for ln in open(bench_json).read().splitlines() if ln.startswith("{")][-1]
+    res = json.loads(line)
+    legs = [(res["config"]["workload"], res["roofline"], res["steps"], res["warmup"])]
+    for key in ("prefill",):
+        if key in res:
+            legs.append((res[key]["workload"], res[key]["roofline"], res[key]["steps"], res[key]["warmup"]))
+    for name, leg in res.get("legs", {}).items():
+        legs.append((name, leg["roofline"], leg["steps"], leg["warmup"]))
+    totals = {}
+    for name, durs in runs:
+        t = totals.setdefault(name, [0, 0.0])
+        t[0] += len(durs)
+        t[1] += sum(durs)
+    grand = sum(t[1] for t in totals.values())
+    top = sorted(totals.items(), key=lambda kv: -kv[1][1])[:12]
+    table = ["| kernel | calls | avg (us) | total (ms) | % GPU time |", "|---|---:|---:|---:|---:|"]
+    for name, (n, tot) in top:
+        table.append(f"| `{name}` | {n} | {tot / n:.2f} | {tot / 1e3:.1f} | {100 * tot / grand:.1f} |")
+    used = set()
+    written = []
+    for workload, roof, steps, warmup in legs:
+        kernel = roof["kernel"]
+        # template arguments name the tile variant in the trace; match on the kernel's base name
+        cand = [i for i, (n, d) in enumerate(runs) if i not in used and re.search(rf"\b{kernel}\b", n)
+                and len(d) == warmup + steps]
+        if not cand:
+            log(f"[summarize] no run of {kernel} with {warmup + steps} launches for {workload}")
+            continue
+        i = cand[0]
+        used.add(i)
+        name, durs = runs[i]
+        timed = durs[-steps:]
+        avg = sum(timed) / len(timed)
+        unit = roof["unit"]
+        work = roof.get("algorithmic_flops_per_launch") if roof["bound"] == "mfma" else roof["algorithmic_bytes_per_launch"]
+        rate = work / (avg * 1e-6) / (1e12 if unit == "TFLOP/s" else 1e9)
+        text = [f"# {kernel} — {workload}", "",
+                "Kernel trace on one MI355X, run from the repository root; the same run printed the bench JSON "
+                "line whose figures are compared below.", "", "```", command, "```", "",
+                f"Kernel `{name}`: {len(durs)} launches in this workload's run (first launch, {warmup - 1} more "
+                f"warm-up, {steps} timed).", "",
+                f"- trace, timed launches: average {avg:.2f} us (min {min(timed):.2f}, max {max(timed):.2f}); "
+                f"first launch {durs[0]:.2f} us",
+                f"- bench.py, same run (HIP events around the timed region / steps): {roof['launch_us']:.2f} us",
+                f"- algorithmic {'FLOPs' if roof['bound'] == 'mfma' else 'bytes'} per launch: {work}",
+                f"- at the trace average: {rate:.1f} {unit} = {100 * rate / roof['peak']:.1f}% of {roof['peak']} {unit}",
+                "", "Top kernels of the whole run:", ""] + table
+        fname = os.path.join(out_dir, f"{kernel}__{workload}.md")
+        with open(fname, "w") as f:
+            f.write("\n".join(text) + "\n")
+        written.append(fname)
+        print(f"{fname}: trace {avg:.2f} us, bench {roof['launch_us']:.2f} us")
+    return written
+
+
 def time_steps(fn_list, steps, warmup, torch, per_launch=False):
     """Run fn_list[i % R]() for warmup + steps and time the last `steps` with
     HIP events on the current stream (the stream the kernels run on).
@@ -417,7 +495,13 @@ def main():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="store HBM bytes per launch from two counter runs (no GPU needed)")
     ap.add_argument("--traffic-command", default="", help="the profiled command, stored with --record-traffic")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "BENCH_JSON"),
+                    help="write profiles/ summaries from a kernel trace of a bench run (no GPU needed)")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.traffic_command, os.path.join(ROOT, "profiles"))
+        return
 
     from workloads import configs
     extra = [int(c) for c in args.extra_configs.split(",") if c.strip()]
