@@ -48,8 +48,8 @@ int prepare_product(const void *x, const void *packed, const void *y, int64_t m,
     } else {
         *kind = kKindGemv;
         *variant = gemv_variant(dtype, m);
-        if (*variant == 2 && p.kg * kTileK > gemv_max_kpad(2)) *variant = 3;
-        if (p.kg * kTileK > gemv_max_kpad(*variant)) return MNB_ERR_SHAPE;
+        if (*variant == 2 && !gemv_lds_fits(p, 2)) *variant = 3;
+        if (!gemv_lds_fits(p, *variant)) return MNB_ERR_SHAPE;
         if (*variant >= 2 && gemv_workgroups(p, *variant) > 0x7FFFFFFFLL) return MNB_ERR_SHAPE;
     }
     *out = p;

@@ -39,16 +39,42 @@ constexpr int kTG = 8;  // tiles per load group: one metadata group
 static_assert(kMetaGroup == kTG, "a load group is one metadata group");
 constexpr int kDecodeOcc = 3;  // decode workgroups per CU (12 waves)
 
-// Scales of TG consecutive tiles, read with one vector load.
+// Buffer resource over [base, base + bytes): loads at or past `bytes` read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+constexpr int kNonTemporal = 2;  // buffer-load cache policy: streamed once, not kept
+
+// A value made wave-uniform (kept in a scalar register).
+__device__ __forceinline__ int uniform_int(int v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_readfirstlane(v);
+#else
+    return v;
+#endif
+}
+
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+#else
+    return v;
+#endif
+}
+
+// Scales of TG consecutive tiles, read with one (float16) or two (float32)
+// 16-byte vector loads.
 template <typename T, int TG>
 struct ScaleVec {
     static constexpr int kWords = TG * (int)sizeof(T) / 4;
-    uint32_t w[kWords];
     static_assert(kWords % 4 == 0, "whole 16-byte loads");
-    __device__ void load(const uint8_t *p) {
+    uint32_t w[kWords];
+    __device__ void load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
 #pragma unroll
         for (int i = 0; i < kWords / 4; ++i) {
-            const u32x4 v = reinterpret_cast<const u32x4 *>(p)[i];
+            const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16 * i, soff, 0));
             w[4 * i + 0] = v.x;
             w[4 * i + 1] = v.y;
             w[4 * i + 2] = v.z;
@@ -72,33 +98,52 @@ struct Group {
     uint32_t z;
 };
 
-// Loads tiles [c0, c0 + kTG) of row group g (tiles past kg are not read);
-// mi is the metadata index of entry e of row group g, tile c0.
+// Loads tiles [c0, c0 + kTG) of row group g: its scales and zero points
+// first (tile 0 needs them), then the codes in tile order, all
+// unconditionally, so that the compiler waits for exactly the loads a tile
+// uses. Codes of tiles past kg read zero (they lie past the row group's
+// buffer range), and their metadata is the layout's zero padding.
+// With valid false every load has an empty range: nothing is read and the
+// group holds zeros (so that the loads need no branch around them).
 template <typename T>
-__device__ __forceinline__ void load_group(const Problem &p, int64_t g, int64_t c0, int lane, int64_t mi,
-                                           Group<T> &G) {
-    const uint8_t *base = p.packed + (g * p.kg + c0) * kTileCodeBytes + lane * 16;
-    const int64_t nt = p.kg - c0;
+__device__ __forceinline__ void load_group(const Problem &p, int64_t g_, int64_t c0_, bool valid, uint32_t lane_code_off,
+                                           uint32_t e, Group<T> &G) {
+    // (every value below is the same in all lanes; read from the problem
+    // descriptor they may sit in vector registers, and a buffer resource must
+    // be scalar, so they are made wave-uniform explicitly)
+    const int64_t g = uniform_i64(g_), c0 = uniform_i64(c0_), kg = uniform_i64(p.kg);
+    const uint8_t *packed = reinterpret_cast<const uint8_t *>(uniform_i64(reinterpret_cast<int64_t>(p.packed)));
+    // the metadata block of (row group g, tile group c0 / 8): entry e's scales
+    // of the 8 tiles at e * 8 elements, its zero points at e * 4 bytes
+    const int64_t entries = uniform_i64(p.nbt) * kTileRows;
+    const int64_t blk = (g * (uniform_i64(p.kgp) / kMetaGroup) + c0 / kMetaGroup) * entries;
+    const __amdgpu_buffer_rsrc_t ms =
+        buffer_over(packed + uniform_i64(p.scales_off) + blk * kMetaGroup * (int64_t)sizeof(T),
+                    valid ? (uint32_t)(entries * kMetaGroup * (int64_t)sizeof(T)) : 0u);
+    const __amdgpu_buffer_rsrc_t mz = buffer_over(packed + uniform_i64(p.zp_off) + blk * (kMetaGroup / 2),
+                                                  valid ? (uint32_t)(entries * (kMetaGroup / 2)) : 0u);
+    G.s.load(ms, e * kMetaGroup * (uint32_t)sizeof(T), 0);
+    G.z = __builtin_amdgcn_raw_buffer_load_b32(mz, e * (kMetaGroup / 2), 0, 0);
+    const __amdgpu_buffer_rsrc_t codes =
+        buffer_over(packed + g * kg * kTileCodeBytes, valid ? (uint32_t)(kg * kTileCodeBytes) : 0u);
 #pragma unroll
-    for (int u = 0; u < kTG; ++u) {
-        if (u < nt) G.codes[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + u * kTileCodeBytes));
-        else G.codes[u] = u32x4{0u, 0u, 0u, 0u};
-    }
-    G.s.load(p.packed + p.scales_off + mi * (int64_t)sizeof(T));
-    G.z = *reinterpret_cast<const uint32_t *>(p.packed + p.zp_off + (mi >> 1));
+    for (int u = 0; u < kTG; ++u)
+        G.codes[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   codes, lane_code_off, (uint32_t)((c0 + u) * kTileCodeBytes),
+                                                   kNonTemporal));
 }
 
 // Contribution of tiles [c0, c0 + kTG) to the lane's partial dot product.
+// Tiles past kg contribute exactly zero: zero codes, scales and zero points
+// against activations staged as zeros.
 template <typename T>
-__device__ __forceinline__ float group_math(const Group<T> &G, int64_t nt, const T *xs, const float *xsum, int64_t c0,
-                                            int j) {
+__device__ __forceinline__ float group_math(const Group<T> &G, const T *xs, const float *xsum, int64_t c0, int j) {
     float acc = 0.0f;
     // the group's first tile in LDS; tile u sits at a constant offset from it
     const T *xg = xs + c0 * kTileK + j * kChunk;
     const float *sg = xsum + c0 * 4 + j;
 #pragma unroll
     for (int u = 0; u < kTG; ++u) {
-        if (u >= nt) break;
         const float s = G.s.get(u);
         const float zs = (float)((G.z >> (4 * u)) & 15u) * sg[u * 4];
         const u32x4 w = G.codes[u];
@@ -132,15 +177,22 @@ __device__ __forceinline__ float group_math(const Group<T> &G, int64_t nt, const
             part -= zs;
         }
         acc = __builtin_fmaf(s, part, acc);
+        // each tile's activation reads stay with its arithmetic: hoisted
+        // ahead of the code loads they would hold 128 more registers
+        __builtin_amdgcn_sched_barrier(0);
     }
     return acc;
 }
 
-// Stage x[0 .. K) (zero-filled to K_pad) and its 32-input chunk sums in LDS.
+// Inputs the decode kernel stages: K padded to whole load groups.
+__host__ __device__ __forceinline__ int64_t decode_staged_k(int64_t kg) { return (kg + kTG - 1) / kTG * kTG * kTileK; }
+
+// Stage x[0 .. K) (zero-filled to whole load groups) and its 32-input chunk
+// sums in LDS.
 template <typename T>
 __device__ __forceinline__ void stage_x(const Problem &p, T *xs, float *xsum) {
     __syncthreads();  // every wave is done with the previous vector
-    const int64_t kp = p.kg * kTileK;
+    const int64_t kp = decode_staged_k(p.kg);
     const T *x = static_cast<const T *>(p.x);
     constexpr int kPer = 16 / sizeof(T);
     for (int64_t i = threadIdx.x; i < kp / kPer; i += kGemvThreads) {
@@ -184,29 +236,32 @@ template <typename T, bool kGrouped, bool kArgmax = false>
 __device__ __forceinline__ uint64_t decode_range(const Problem *entries, Problem p, int pi, int64_t b0, int64_t b1,
                                                  uint8_t *smem) {
     uint64_t best = 0;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = uniform_int((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
     const int r = lane & 15, j = lane >> 4;
+    const uint32_t lane_code_off = (uint32_t)lane * 16u;
     int64_t b = b0;
     while (b < b1) {
         if constexpr (kGrouped) {
             while (b >= p.batch_end) p = entries[++pi];
         }
         const int64_t bend = b1 < p.batch_end ? b1 : p.batch_end;
-        const int64_t kp = p.kg * kTileK;
+        const int64_t kp = decode_staged_k(p.kg);
         T *xs = reinterpret_cast<T *>(smem);
         float *xsum = reinterpret_cast<float *>(smem + kp * sizeof(T));
-        const int e = (j / (p.bs / kChunk)) * kTileRows + r;
+        const uint32_t e = (uint32_t)((j / (p.bs / kChunk)) * kTileRows + r);
         const int64_t ngroups = (p.kg + kTG - 1) / kTG;
 
         int64_t sb = b, g = (b - p.batch_begin) * kGemvWaves + wave;
         int64_t c0 = 0;
-        bool have = g < p.rg;
+        const bool have = g < p.rg;
         Group<T> cur;
+        // the first weight group is in flight while x is staged
+        load_group<T>(p, g, 0, have, lane_code_off, e, cur);
         stage_x<T>(p, xs, xsum);
 
         float acc = 0.0f;
-        int64_t mi_row = 0;  // metadata index of entry e, tile 0 of row group g
         while (have) {
+            acc += group_math<T>(cur, xs, xsum, c0, j);
             // the step after this one: next 8 tiles, or the next batch's row group
             int64_t nb = sb, nc0 = c0 + kTG;
             if (nc0 >= ngroups * kTG) {
@@ -215,10 +270,7 @@ __device__ __forceinline__ uint64_t decode_range(const Problem *entries, Problem
             }
             const int64_t ng = (nb - p.batch_begin) * kGemvWaves + wave;
             const bool nvalid = nb < bend && ng < p.rg;
-            if (c0 == 0) mi_row = meta_index(g, p.nbt, p.kgp, e, 0);
-            load_group<T>(p, g, c0, lane, mi_row + (c0 / kMetaGroup) * (p.nbt * kTileRows * kMetaGroup) + c0 % kMetaGroup,
-                          cur);
-            acc += group_math<T>(cur, p.kg - c0, xs, xsum, c0, j);
+            load_group<T>(p, ng, nc0, nvalid, lane_code_off, e, cur);
             if (nc0 == 0) {  // row group finished
                 float v = acc;
                 v += __shfl_xor(v, 16);
@@ -419,15 +471,12 @@ static int elem_bytes(int variant) { return variant == 0 ? 2 : 4; }
 static int rows_per_pass(int variant) { return variant == 2 ? kRowsMR : 1; }
 
 size_t gemv_lds_bytes(const Problem &p, int variant) {
-    const int64_t kp = p.kg * kTileK;
-    if (variant >= 2) return (size_t)(rows_per_pass(variant) * kp * 4);
+    if (variant >= 2) return (size_t)(rows_per_pass(variant) * p.kg * kTileK * 4);
+    const int64_t kp = decode_staged_k(p.kg);
     return (size_t)(kp * elem_bytes(variant) + kp / kChunk * 4);
 }
 
-int64_t gemv_max_kpad(int variant) {
-    if (variant >= 2) return kGemvMaxLds / (rows_per_pass(variant) * 4);
-    return (int64_t)(kGemvMaxLds / (elem_bytes(variant) + 4.0 / kChunk));
-}
+bool gemv_lds_fits(const Problem &p, int variant) { return gemv_lds_bytes(p, variant) <= (size_t)kGemvMaxLds; }
 
 int64_t gemv_workgroups(const Problem &p, int variant) {
     const int mr = rows_per_pass(variant);

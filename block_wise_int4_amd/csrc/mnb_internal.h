@@ -108,7 +108,7 @@ hipError_t launch_dequant(const uint8_t *packed, const Layout &L, int dtype, voi
 // (fp32, M >= 2). Variants: 0 = fp16 decode, 1 = fp32 decode, 2 = fp32 rows.
 int gemv_variant(int dtype, int64_t m);
 int64_t gemv_workgroups(const Problem &p, int variant);   // the fp32 rows variants (2, 3)
-int64_t gemv_max_kpad(int variant);
+bool gemv_lds_fits(const Problem &p, int variant);  // its staged activations fit the LDS of a CU
 size_t gemv_lds_bytes(const Problem &p, int variant);
 // Decode schedule for a list of problems (host): fills batch_begin/end of
 // each problem and the workgroup table; returns the workgroup count.
