@@ -125,7 +125,6 @@ def summarize_trace(trace_csv, bench_json, command, out_dir):
     of its kernel; runs of one kernel are matched to workloads in the order
     bench.py times them."""
     import csv
-    import re
 
     rows = list(csv.DictReader(open(trace_csv)))
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
@@ -159,9 +158,8 @@ def summarize_trace(trace_csv, bench_json, command, out_dir):
     written = []
     for workload, roof, steps, warmup in legs:
         kernel = roof["kernel"]
-        # template arguments name the tile variant in the trace; match on the kernel's base name
-        cand = [i for i, (n, d) in enumerate(runs) if i not in used and re.search(rf"\b{kernel}\b", n)
-                and len(d) == warmup + steps]
+        # (template arguments name the tile variant in the trace; match on the kernel's base name)
+        cand = [i for i, (n, d) in enumerate(runs) if i not in used and kernel in n and len(d) == warmup + steps]
         if not cand:
             log(f"[summarize] no run of {kernel} with {warmup + steps} launches for {workload}")
             continue
@@ -189,7 +187,142 @@ def summarize_trace(trace_csv, bench_json, command, out_dir):
             f.write("\n".join(text) + "\n")
         written.append(fname)
         print(f"{fname}: trace {avg:.2f} us, bench {roof['launch_us']:.2f} us")
+    # the next-row lines of the headline workload: the fused LM-head argmax
+    # (two kernels per call, alternating) and the embedding gather
+    def last(name_part, n):
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows if name_part in r["Kernel_Name"]]
+        return d[-n:] if len(d) >= n else None
+    steps = res["steps"]
+    head_name = res["config"]["workload"]
+    if "lm_head_argmax" in res:
+        la = res["lm_head_argmax"]
+        fused, finish = last("decode_argmax_kernel", steps), last("argmax_finish_kernel", steps)
+        if fused and finish:
+            f_avg, g_avg = sum(fused) / steps, sum(finish) / steps
+            text = [f"# decode_argmax_kernel — {head_name} LM head", "",
+                    "Kernel trace on one MI355X, run from the repository root; the same run printed the bench "
+                    "JSON line whose lm_head_argmax figures are compared below.", "", "```", command, "```", "",
+                    f"LM head {la['shape'][0]} x {la['shape'][1]}, the last {steps} calls of each kernel:", "",
+                    f"- `decode_argmax_kernel` (the product with per-workgroup argmax slots): {f_avg:.2f} us",
+                    f"- `argmax_finish_kernel` (reduces the slots): {g_avg:.2f} us",
+                    f"- bench.py, same run, time per fused call (both launches, back to back): "
+                    f"{la['fused_argmax']['us_per_call']} us; the plain product that writes the logits: "
+                    f"{la['plain_gemv']['us_per_call']} us",
+                    f"- algorithmic bytes per fused call: {la['fused_argmax']['algorithmic_bytes']}"]
+            fname = os.path.join(out_dir, f"decode_argmax_kernel__{head_name}-lm-head.md")
+            with open(fname, "w") as f:
+                f.write("\n".join(text) + "\n")
+            written.append(fname)
+            print(f"{fname}: {f_avg:.2f} + {g_avg:.2f} us")
+    if "embedding_gather" in res:
+        eg = res["embedding_gather"]
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows
+             if "embed_gather_kernel" in r["Kernel_Name"]]
+        keys = [k for k in eg if k.startswith("tokens_")]
+        per = len(d) // max(len(keys), 1)
+        if keys and per >= steps:
+            text = [f"# embed_gather_kernel — {head_name} embedding rows", "",
+                    "Kernel trace on one MI355X, run from the repository root; the same run printed the bench "
+                    "JSON line whose embedding_gather figures are compared below.", "", "```", command, "```", "",
+                    f"Table {eg['vocab']} x {eg['hidden']} int8, {eg['out']} out; the last {steps} calls of each "
+                    "size:", "", "| rows | trace avg (us) | bench us per call | algorithmic bytes | GB/s (trace) |",
+                    "|---:|---:|---:|---:|---:|"]
+            for i, k in enumerate(keys):
+                seg = d[i * per:(i + 1) * per][-steps:]
+                avg = sum(seg) / len(seg)
+                text.append(f"| {k.split('_')[1]} | {avg:.2f} | {eg[k]['us_per_call']} | {eg[k]['algorithmic_bytes']} "
+                            f"| {eg[k]['algorithmic_bytes'] / (avg * 1e-6) / 1e9:.1f} |")
+            fname = os.path.join(out_dir, f"embed_gather_kernel__{head_name}-embedding.md")
+            with open(fname, "w") as f:
+                f.write("\n".join(text) + "\n")
+            written.append(fname)
+            print(f"{fname}: written")
     return written
+
+
+def summarize_counters(counter_csv, bench_json, timing_json, command, out_path):
+    """MFMA counters of the prefill kernel for profiles/: from a rocprofv3
+    --pmc run (SQ_INSTS_MFMA, SQ_INSTS_VALU_MFMA_MOPS_F16,
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, GRBM_GUI_ACTIVE, GRBM_COUNT) of
+    a bench run and that run's JSON line, per MFMA workload: the MFMA flops
+    the counters count against the algorithmic flops, and the matrix pipes'
+    busy fraction while the GPU is active. The clock comes from the launch
+    time of the same workload in `timing_json`, a bench run without counters
+    (counter collection serializes launches and inflates their times)."""
+    import csv
+
+    disp = {}
+    for r in csv.DictReader(open(counter_csv)):
+        if "gemm_grouped_kernel" not in r["Kernel_Name"]:
+            continue
+        d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    runs = []
+    for k in sorted(disp):
+        if runs and runs[-1][0] == disp[k]["name"] and runs[-1][2] == k - 1:
+            runs[-1][1].append(disp[k])
+            runs[-1][2] = k
+        else:
+            runs.append([disp[k]["name"], [disp[k]], k])
+    line = [ln for ln in open(bench_json).read().splitlines() if ln.startswith("{")][-1]
+    res = json.loads(line)
+    legs = [(res["config"]["workload"], res["roofline"], res["steps"], res["warmup"])]
+    if "prefill" in res:
+        legs.append((res["prefill"]["workload"], res["prefill"]["roofline"], res["prefill"]["steps"],
+                     res["prefill"]["warmup"]))
+    for name, leg in res.get("legs", {}).items():
+        legs.append((name, leg["roofline"], leg["steps"], leg["warmup"]))
+    cus, simds = 256, 4
+    tline = [ln for ln in open(timing_json).read().splitlines() if ln.startswith("{")][-1]
+    tres = json.loads(tline)
+    launch_us = {tres["config"]["workload"]: tres["roofline"]["launch_us"]}
+    if "prefill" in tres:
+        launch_us[tres["prefill"]["workload"]] = tres["prefill"]["roofline"]["launch_us"]
+    for name, leg in tres.get("legs", {}).items():
+        launch_us[name] = leg["roofline"]["launch_us"]
+    text = ["# gemm_grouped_kernel — MFMA counters", "",
+            "rocprofv3 counters of the prefill (MFMA) kernel, one MI355X, run from the repository root. Each "
+            "value is per launch (the same in every timed launch). The clock column is GRBM_GUI_ACTIVE per XCD "
+            "over the launch time bench.py measured for the same workload in a run without counters (counter "
+            "collection serializes launches and inflates their times); the TFLOP/s column is that run's.", "",
+            "```", command, "```", "",
+            "Derivations: one `v_mfma_f32_16x16x32_f16` is 16384 flops, so MFMA flops = SQ_INSTS_MFMA x 16384 "
+            "(and SQ_INSTS_VALU_MFMA_MOPS_F16 x 512 gives the same); the matrix pipes' busy fraction = "
+            "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 256 CUs x 4 SIMDs), i.e. the share of "
+            "the GPU-active cycles in which an MFMA occupies a SIMD's matrix pipe.", "",
+            "| workload | kernel | SQ_INSTS_MFMA | MFMA flops / algorithmic | MFMA_MOPS_F16 x 512 / MFMA flops | "
+            "SQ_VALU_MFMA_BUSY_CYCLES | GRBM_GUI_ACTIVE | busy fraction | clock (GHz) | TFLOP/s |",
+            "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    used = set()
+    for workload, roof, steps, warmup in legs:
+        if roof["bound"] != "mfma":
+            continue
+        cand = [i for i, (n, d, _) in enumerate(runs) if i not in used and len(d) == warmup + steps]
+        if not cand:
+            log(f"[summarize] no counter run with {warmup + steps} launches for {workload}")
+            continue
+        i = cand[0]
+        used.add(i)
+        name, ds, _ = runs[i]
+        d = ds[-1]
+        flops = d["SQ_INSTS_MFMA"] * 16384
+        gui = d["GRBM_GUI_ACTIVE"] / 8
+        busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * cus * simds)
+        t_us = launch_us.get(workload)
+        clock = gui / (t_us * 1e-6) / 1e9 if t_us else float("nan")
+        tflops = roof["algorithmic_flops_per_launch"] / (t_us * 1e-6) / 1e12 if t_us else float("nan")
+        short = name.split("(")[0].replace("void mnb::", "")
+        text.append(f"| {workload} | `{short}` | {d['SQ_INSTS_MFMA']:.0f} | "
+                    f"{flops / roof['algorithmic_flops_per_launch']:.4f} | "
+                    f"{d['SQ_INSTS_VALU_MFMA_MOPS_F16'] * 512 / flops:.4f} | {d['SQ_VALU_MFMA_BUSY_CYCLES']:.0f} | "
+                    f"{d['GRBM_GUI_ACTIVE']:.0f} | {busy:.3f} | {clock:.2f} | {tflops:.1f} |")
+    text += ["", "MFMA flops above the algorithmic ones are the M padding of the last row tile (for example "
+             "416 / 410 rows). The busy fraction is the MFMA utilisation at the clock the GPU actually ran; "
+             "against the 2.5 PFLOP/s peak, which assumes 2.4 GHz, the roofline fraction is lower by the clock "
+             "ratio. Under the heaviest MFMA load the clock settles lowest."]
+    with open(out_path, "w") as f:
+        f.write("\n".join(text) + "\n")
+    print("\n".join(text))
 
 
 def time_steps(fn_list, steps, warmup, torch, per_launch=False):
@@ -495,9 +628,16 @@ def main():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="store HBM bytes per launch from two counter runs (no GPU needed)")
     ap.add_argument("--traffic-command", default="", help="the profiled command, stored with --record-traffic")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("COUNTER_CSV", "BENCH_JSON", "TIMING_JSON"),
+                    help="write the MFMA counter summary for profiles/ from a --pmc run of bench (no GPU needed)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "BENCH_JSON"),
                     help="write profiles/ summaries from a kernel trace of a bench run (no GPU needed)")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.traffic_command,
+                           os.path.join(ROOT, "profiles", "gemm_grouped_kernel__mfma-counters.md"))
+        return
 
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, args.traffic_command, os.path.join(ROOT, "profiles"))
