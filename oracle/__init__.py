@@ -37,6 +37,12 @@ notes. The functions and what pins each one (tests/test_oracle_pins.py):
                       merged-decoder page
   greedy_argmax,
   embedding_dequant   pinned: brute force and closed forms (see the module)
+  quantize_activations_i8
+                      pinned: exact-rational division with an independent
+                      float32 rounding routine, ties, extreme and all-zero
+                      blocks, round-trip bound
+  matmul_nbits_i8     pinned: equality with matmul_nbits where the int8
+                      activations are exact, Fraction-exact tiny shapes
 """
 
 from .mnb_oracle import (  # noqa: F401
@@ -57,4 +63,7 @@ from .mnb_oracle import (  # noqa: F401
     packed_nbytes,
     greedy_argmax,
     embedding_dequant,
+    A8_QMAX,
+    quantize_activations_i8,
+    matmul_nbits_i8,
 )

@@ -216,6 +216,63 @@ def within_tolerance(y, y_ref, tol):
 
 
 # ---------------------------------------------------------------------------
+# Int8 compute mode: activations quantized per block, integer dot products.
+# ---------------------------------------------------------------------------
+
+A8_QMAX = 127  # largest magnitude of a symmetric int8 activation code
+
+
+def quantize_activations_i8(x, block_size):
+    """Activations X[M, K] as symmetric int8 per (row, block of bs inputs).
+
+    The conversions set an accuracy level of 4 ("Qwen3-ASR-0.6B ONNX for the
+    browser", section "Pick a variant"; "sherpa-onnx STT int4", section
+    "whisper-small") and the pages never say what it computes. Read as the
+    int8 compute setting of MatMulNBits: each activation block is quantized
+    symmetrically with the weights' block size, and the dot products run on
+    integers. Per block, in float32 arithmetic (the precision the kernel
+    takes these decisions in):
+
+      1. amax = max |x| over the block            (exact in float32)
+      2. a_s  = amax / 127                        (one float32 division, RNE)
+      3. qa   = clamp(rint(x / a_s), -127, 127)   (x / a_s one float32 division)
+    A block with amax = 0 gets a_s = 0 and qa = 0.
+
+    Returns (qa int8 [M, K], a_s float32 [M, K/bs]).
+    """
+    x32 = np.asarray(x).astype(np.float32)
+    m, k = x32.shape
+    nb = _blocks(k, block_size)
+    xb = x32.reshape(m, nb, block_size)
+    amax = np.max(np.abs(xb), axis=2)
+    a_s = (amax / np.float32(A8_QMAX)).astype(np.float32)
+    safe = np.where(a_s > 0, a_s, np.float32(1))
+    ratio = (xb / safe[:, :, None]).astype(np.float32)   # float32 operands: a float32 division
+    qa = np.where(a_s[:, :, None] > 0, np.rint(ratio), 0.0)
+    qa = np.clip(qa, -A8_QMAX, A8_QMAX).astype(np.int8).reshape(m, k)
+    return qa, a_s
+
+
+def matmul_nbits_i8(x, q, zero_points, scales, block_size):
+    """Y[M, N] in the int8 compute mode:
+
+      Y[m, n] = sum_b s[n, b] * a_s[m, b] * sum_{k in b} (q[n, k] - zp[n, b]) * qa[m, k]
+
+    with (qa, a_s) = quantize_activations_i8(X). The integer block sums are
+    exact (int64); scaling and the sum over blocks are float64.
+    """
+    qa, a_s = quantize_activations_i8(x, block_size)
+    m, k = qa.shape
+    n = np.asarray(q).shape[0]
+    nb = _blocks(k, block_size)
+    w = np.asarray(q).astype(np.int64) - np.repeat(np.asarray(zero_points).astype(np.int64), block_size, axis=1)
+    isum = np.einsum("mbk,nbk->mnb", qa.astype(np.int64).reshape(m, nb, block_size),
+                     w.reshape(n, nb, block_size))
+    s = np.asarray(scales).astype(np.float64)
+    return np.sum(isum.astype(np.float64) * a_s.astype(np.float64)[:, None, :] * s[None, :, :], axis=2)
+
+
+# ---------------------------------------------------------------------------
 # Storage accounting.
 # ---------------------------------------------------------------------------
 

@@ -492,3 +492,110 @@ def test_symmetric_round_trip_bound(dtype, u):
     d = oracle.dequantize_exact(q, zp, s, 64)
     err = np.abs(w.astype(np.float64) - d).reshape(40, 4, 64).max(axis=2)
     assert (err <= s.astype(np.float64) * (0.5 + 7 * u)).all()
+
+
+# ---------------------------------------------------------------------------
+# Int8 compute mode: activation quantizer and the integer-dot product.
+# ---------------------------------------------------------------------------
+
+def rint_half_even(fr):
+    """Nearest integer to a Fraction, ties to even."""
+    fl = fr.numerator // fr.denominator
+    rem = fr - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return fl
+
+
+def a8_reference(block):
+    """One block of float32 activations -> (scale, codes), from exact
+    rationals and the integer float32 rounding routine above."""
+    vals = [frac(v) for v in block]
+    amax = max(abs(v) for v in vals)
+    scale = rne(amax / 127, np.float32)
+    if scale == 0:
+        return Fraction(0), [0] * len(vals)
+    codes = [max(-127, min(127, rint_half_even(rne(v / scale, np.float32)))) for v in vals]
+    return scale, codes
+
+
+@pytest.mark.parametrize("f16,bs", [(True, 32), (False, 32), (True, 64), (False, 128)])
+def test_a8_quantizer_against_exact_rationals(f16, bs):
+    rng = np.random.default_rng(bs + 3 * f16)
+    x = rng.standard_normal((3, 2 * bs)).astype(np.float16 if f16 else np.float32)
+    x[1, :bs] *= 1e-3           # a small-magnitude block
+    x[2, bs:] = 0.0             # an all-zero block
+    qa, a_s = oracle.quantize_activations_i8(x, bs)
+    assert qa.dtype == np.int8 and a_s.dtype == np.float32 and a_s.shape == (3, 2)
+    for m in range(3):
+        for b in range(2):
+            scale, codes = a8_reference(x[m, b * bs:(b + 1) * bs])
+            assert frac(a_s[m, b]) == scale
+            assert [int(c) for c in qa[m, b * bs:(b + 1) * bs]] == codes
+
+
+def test_a8_extremes_ties_and_zero_block():
+    bs = 32
+    x = np.zeros((2, 2 * bs), dtype=np.float32)
+    # amax = 127/8 gives the exact scale 1/8: the extremes are +-127 and
+    # quotients k + 1/2 round to even
+    x[0, 0] = 127 / 8
+    x[0, 1] = -127 / 8
+    x[0, 2] = 2.5 / 8
+    x[0, 3] = 3.5 / 8
+    x[0, 4] = -2.5 / 8
+    x[0, 5] = 0.5 / 8
+    qa, a_s = oracle.quantize_activations_i8(x, bs)
+    assert a_s[0, 0] == np.float32(1 / 8)
+    assert list(qa[0, :6]) == [127, -127, 2, 4, -2, 0]
+    assert a_s[0, 1] == 0 and a_s[1, 0] == 0 and not qa[1].any() and not qa[0, bs:].any()
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+def test_a8_round_trip_bound(bs):
+    rng = np.random.default_rng(40 + bs)
+    x = (rng.standard_normal((8, 4 * bs)) * rng.choice([1e-3, 1.0, 30.0], size=(8, 1))).astype(np.float32)
+    qa, a_s = oracle.quantize_activations_i8(x, bs)
+    s = np.repeat(a_s.astype(np.float64), bs, axis=1)
+    err = np.abs(x.astype(np.float64) - qa.astype(np.float64) * s)
+    # half a step, plus the float32 roundings of the scale and of the quotient
+    assert np.all(err <= s * (0.5 + 127 * 2.0 ** -22))
+    assert np.all(np.abs(qa.astype(np.int64)) <= 127)
+
+
+def test_a8_product_equals_plain_product_when_activations_are_exact():
+    """Blocks whose largest magnitude is 127 * 2^-e and whose values are
+    multiples of 2^-e quantize exactly, so the int8 product is the plain
+    product (pinned on its own) computed another way."""
+    rng = np.random.default_rng(9)
+    m, n, bs, nb = 3, 5, 32, 4
+    k = bs * nb
+    codes = rng.integers(-127, 128, size=(m, k))
+    codes[:, ::bs] = 127                      # every block reaches 127
+    e = rng.integers(2, 9, size=(m, nb))
+    x = (codes * np.repeat(2.0 ** -e, bs, axis=1)).astype(np.float32)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    q, s, zp = oracle.rtn_quantize(w, bs, np.float16)
+    y8 = oracle.matmul_nbits_i8(x, q, zp, s, bs)
+    y = oracle.matmul_nbits(x, q, zp, s, bs)
+    assert np.array_equal(y8, y)
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+def test_a8_product_against_fractions(bs):
+    rng = np.random.default_rng(77 + bs)
+    m, n, k = 2, 3, 2 * bs
+    x = rng.standard_normal((m, k)).astype(np.float16)
+    q = rng.integers(0, 16, size=(n, k), dtype=np.uint8)
+    zp = rng.integers(0, 16, size=(n, k // bs), dtype=np.uint8)
+    s = (rng.random((n, k // bs)) * 0.01 + 1e-4).astype(np.float16)
+    y = oracle.matmul_nbits_i8(x, q, zp, s, bs)
+    for i in range(m):
+        blocks = [a8_reference(x[i, b * bs:(b + 1) * bs]) for b in range(k // bs)]
+        for jn in range(n):
+            exact = Fraction(0)
+            for b, (scale, codes) in enumerate(blocks):
+                isum = sum((int(q[jn, b * bs + t]) - int(zp[jn, b])) * codes[t] for t in range(bs))
+                exact += frac(s[jn, b]) * scale * isum
+            # float64 scaling and sum over two blocks: within a few roundings
+            assert abs(frac(y[i, jn]) - exact) <= abs(exact) * 2 ** -50 + Fraction(1, 2 ** 80)
