@@ -14,11 +14,14 @@ from .mnb import (  # noqa: F401
     mnb_abi_version,
     mnb_dequant,
     mnb_gemm,
+    mnb_gemm_i8,
+    mnb_gemm_i8_workspace_bytes,
     mnb_gemm_grouped,
     mnb_gemv,
     mnb_pack,
     mnb_packed_bytes,
     mnb_plan_grouped,
+    mnb_quantize_act_i8,
     mnb_quantize_rtn,
     mnb_status_string,
     mnb_unpack,

@@ -133,6 +133,37 @@ int mnb_gemm(const void *x, const void *packed, void *y, int64_t M, int64_t N, i
     return hip_status(launch_gemv(p, dtype, variant, as_stream(stream)));
 }
 
+size_t mnb_gemm_i8_workspace_bytes(int64_t M, int64_t K, int block_size) {
+    if (check_format(1, K, 4, block_size, MNB_F32) != MNB_OK) return 0;
+    if (M <= 0 || M > MNB_MAX_ROWS) return 0;
+    return (size_t)a8_workspace_bytes(M, K, block_size);
+}
+
+int mnb_quantize_act_i8(const void *x, int64_t M, int64_t K, int block_size, int dtype, int8_t *qa, float *scales,
+                        void *stream) {
+    if (!x || !qa || !scales) return MNB_ERR_NULL;
+    int st = check_format(1, K, 4, block_size, dtype);
+    if (st) return st;
+    if (M <= 0 || M > MNB_MAX_ROWS) return MNB_ERR_SHAPE;
+    if ((M * (K / 8) + 255) / 256 > 0x7FFFFFFFLL) return MNB_ERR_SHAPE;
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(qa) & 7) || (reinterpret_cast<uintptr_t>(scales) & 3))
+        return MNB_ERR_ALIGN;
+    return hip_status(launch_quantize_act(x, M, K, block_size, dtype, qa, scales, as_stream(stream)));
+}
+
+int mnb_gemm_i8(const void *x, const void *packed, void *y, void *workspace, size_t workspace_bytes, int64_t M,
+                int64_t N, int64_t K, int bits, int block_size, int dtype, void *stream) {
+    if (!x || !packed || !y || !workspace) return MNB_ERR_NULL;
+    int st = check_format(N, K, bits, block_size, dtype);
+    if (st) return st;
+    if (M <= 0 || M > MNB_MAX_ROWS) return MNB_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(packed) || !aligned16(y) || !aligned16(workspace)) return MNB_ERR_ALIGN;
+    if (workspace_bytes < (size_t)a8_workspace_bytes(M, K, block_size)) return MNB_ERR_INVALID;
+    const Problem p = make_problem(x, packed, y, M, N, K, block_size, dtype_bytes(dtype));
+    if ((M * (K / 8) + 255) / 256 > 0x7FFFFFFFLL || gemm_i8_workgroups(p) > 0x7FFFFFFFLL) return MNB_ERR_SHAPE;
+    return hip_status(launch_gemm_i8(p, dtype, workspace, as_stream(stream)));
+}
+
 int mnb_embed_gather(const int8_t *table, const float *row_scales, const int64_t *ids, int64_t T, int64_t V,
                      int64_t H, int dtype, void *out, void *stream) {
     if (!table || !row_scales || !ids || !out) return MNB_ERR_NULL;

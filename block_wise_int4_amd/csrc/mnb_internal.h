@@ -127,6 +127,14 @@ hipError_t argmax_scratch(void **slots, int64_t *n_slots);
 hipError_t launch_gemv_grouped(const Problem *dev_entries, int count, const GemvWg *dev_table, int64_t wgs,
                                int variant, size_t lds, hipStream_t st);
 
+// Int8 compute mode: activations quantized per block to int8 (the caller's
+// workspace holds them), integer dot products with the 4-bit codes.
+int64_t a8_workspace_bytes(int64_t m, int64_t k, int bs);
+int64_t gemm_i8_workgroups(const Problem &p);
+hipError_t launch_quantize_act(const void *x, int64_t m, int64_t k, int bs, int dtype, int8_t *qa, float *scales,
+                               hipStream_t st);
+hipError_t launch_gemm_i8(const Problem &p, int dtype, void *workspace, hipStream_t st);
+
 // MFMA kernel: fp16 with M >= 2.
 int gemm_variant(int64_t m);
 void gemm_tiles(const Problem &p, int variant, int32_t *tiles_m, int32_t *tiles_n);

@@ -56,6 +56,9 @@ _SIGNATURES = {
     "mnb_gemv_argmax_noalloc": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
     "mnb_embed_gather": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _vp]),
     "mnb_gemm": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp]),
+    "mnb_gemm_i8_workspace_bytes": (_sz, [_i64, _i64, _int]),
+    "mnb_quantize_act_i8": (_int, [_vp, _i64, _i64, _int, _int, _vp, _vp, _vp]),
+    "mnb_gemm_i8": (_int, [_vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _int, _int, _int, _vp]),
     "mnb_plan_bytes": (_sz, [_int]),
     "mnb_plan_grouped": (_int, [ctypes.POINTER(mnb_problem), _int, _int, _int, _int, _vp, _sz]),
     "mnb_plan_launches": (_int, [_vp]),
@@ -382,3 +385,51 @@ def mnb_gemm_grouped(plan):
     _check("mnb_gemm_grouped", lib().mnb_gemm_grouped(
         ctypes.c_void_p(plan.host.data_ptr()), _dev(plan.device, "plan_device"), _stream(plan.device.device)))
     return plan.outputs
+
+
+def mnb_gemm_i8_workspace_bytes(M, K, block_size):
+    return lib().mnb_gemm_i8_workspace_bytes(M, K, block_size)
+
+
+def i8_workspace(M, K, block_size, device):
+    """A workspace for mnb_gemm_i8 with M rows of K inputs (reusable by calls
+    of at most that size that run one after another on one stream)."""
+    nbytes = mnb_gemm_i8_workspace_bytes(M, K, block_size)
+    if nbytes == 0:
+        raise ValueError(f"no int8 workspace for M={M}, K={K}, block_size={block_size}")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def mnb_quantize_act_i8(x, block_size):
+    """(qa int8 [M, K], a_s float32 [M, K/bs]): the int8 compute mode's
+    per-block symmetric activation quantizer."""
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    qa = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    a_s = torch.empty((M, K // block_size), dtype=torch.float32, device=x.device)
+    _check("mnb_quantize_act_i8", lib().mnb_quantize_act_i8(
+        _dev(x, "x"), M, K, block_size, dtype_code(x.dtype), _dev(qa, "qa"), _dev(a_s, "scales"),
+        _stream(x.device)))
+    return qa, a_s
+
+
+def mnb_gemm_i8(x, pw, workspace=None, y=None):
+    """Y[M, N] in the int8 compute mode: X quantized per block to int8, then
+    integer dot products with the 4-bit codes (any M >= 1)."""
+    _check_x(x, pw)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M = x.shape[0]
+    if workspace is None:
+        workspace = i8_workspace(M, pw.K, pw.block_size, x.device)
+    if workspace.device != x.device:
+        raise ValueError(f"workspace is on {workspace.device}, not {x.device}")
+    if y is None:
+        y = torch.empty((M, pw.N), dtype=pw.dtype, device=x.device)
+    _check_buf(y, "y", pw.dtype, M * pw.N, x.device)
+    _check("mnb_gemm_i8", lib().mnb_gemm_i8(
+        _dev(x, "x"), _dev(pw.packed, "packed"), _dev(y, "y"), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), M, pw.N, pw.K, pw.bits, pw.block_size,
+        dtype_code(pw.dtype), _stream(x.device)))
+    return y

@@ -239,6 +239,39 @@ int mnb_gemm(const void *x, const void *packed, void *y,
              int64_t M, int64_t N, int64_t K, int bits, int block_size, int dtype, void *stream);
 
 /*
+ * Int8 compute mode. The published int4 exports set an accuracy level of 4
+ * ("Qwen3-ASR-0.6B ONNX for the browser", section "Pick a variant";
+ * "sherpa-onnx STT int4", section "whisper-small"), read here as
+ * MatMulNBits' int8 compute setting: the activations are quantized per
+ * (row, block of block_size inputs) to symmetric int8, in float32,
+ *   a_s = amax / 127,  qa = clamp(rint(x / a_s), -127, 127)
+ * (round to nearest even; a block of zeros gets a_s = 0, qa = 0), and
+ *   Y[m][n] = sum_b s[n][b] * a_s[m][b] * sum_{k in b} (q[n][k] - zp[n][b]) * qa[m][k],
+ * the block sums exact in integers, the scaling and the sum over blocks in
+ * float32, rounded once to dtype.
+ *
+ * mnb_gemm_i8_workspace_bytes: device workspace mnb_gemm_i8 needs for M
+ * rows of K inputs (quantized activations, their scales and chunk sums);
+ * 0 if the arguments are invalid.
+ *
+ * mnb_quantize_act_i8: the quantizer alone (for tests and for callers that
+ * keep quantized activations). x: device [M][K] dtype; qa: device int8
+ * [M][K] (8-byte aligned); scales: device float32 [M][K / block_size].
+ *
+ * mnb_gemm_i8: the product, any M >= 1. x, y: device row-major [M][K],
+ * [M][N] dtype; packed: mnb_pack output; workspace: device, 16-byte
+ * aligned, at least mnb_gemm_i8_workspace_bytes(M, K, block_size) bytes
+ * (MNB_ERR_INVALID if workspace_bytes is smaller); its contents are
+ * overwritten and it must not be shared by calls that may overlap. Two
+ * launches on `stream` (quantize, product); nothing is allocated.
+ */
+size_t mnb_gemm_i8_workspace_bytes(int64_t M, int64_t K, int block_size);
+int mnb_quantize_act_i8(const void *x, int64_t M, int64_t K, int block_size, int dtype, int8_t *qa, float *scales,
+                        void *stream);
+int mnb_gemm_i8(const void *x, const void *packed, void *y, void *workspace, size_t workspace_bytes,
+                int64_t M, int64_t N, int64_t K, int bits, int block_size, int dtype, void *stream);
+
+/*
  * Grouped execution: many independent products in one launch per kernel
  * class (one for the M = 1 problems, one for the M >= 2 problems). All
  * problems of a plan share bits, block_size and dtype.

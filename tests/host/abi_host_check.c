@@ -90,6 +90,22 @@ static void check_invalid_calls(void) {
                            NULL) == MNB_ERR_SHAPE);
     CHECK(mnb_embed_gather((const int8_t *)w, (const float *)x, (const int64_t *)ws, 0, 100, 16, MNB_F16, y,
                            NULL) == MNB_OK);
+    /* int8 compute mode */
+    const size_t wsb = mnb_gemm_i8_workspace_bytes(4, 128, 32);
+    CHECK(wsb >= 4 * 128 && wsb % 256 == 0);
+    CHECK(mnb_gemm_i8_workspace_bytes(410, 2048, 64) >= (size_t)(410 * 2048 + 410 * 32 * 4 + 410 * 64 * 4));
+    CHECK(mnb_gemm_i8_workspace_bytes(0, 128, 32) == 0);
+    CHECK(mnb_gemm_i8_workspace_bytes(4, 100, 32) == 0);
+    CHECK(mnb_gemm_i8_workspace_bytes(4, 128, 48) == 0);
+    CHECK(mnb_gemm_i8(x, w, y, NULL, wsb, 4, 64, 128, 4, 32, MNB_F16, NULL) == MNB_ERR_NULL);
+    CHECK(mnb_gemm_i8(x, w, y, ws, wsb - 1, 4, 64, 128, 4, 32, MNB_F16, NULL) == MNB_ERR_INVALID);
+    CHECK(mnb_gemm_i8(x, w, y, (char *)ws + 8, wsb, 4, 64, 128, 4, 32, MNB_F16, NULL) == MNB_ERR_ALIGN);
+    CHECK(mnb_gemm_i8(x, w, y, ws, wsb, 4, 64, 100, 4, 32, MNB_F16, NULL) == MNB_ERR_SHAPE);
+    CHECK(mnb_gemm_i8(x, w, y, ws, wsb, 0, 64, 128, 4, 32, MNB_F16, NULL) == MNB_ERR_SHAPE);
+    CHECK(mnb_gemm_i8(x, w, y, ws, wsb, 4, 64, 128, 4, 32, 5, NULL) == MNB_ERR_DTYPE);
+    CHECK(mnb_quantize_act_i8(x, 4, 128, 32, MNB_F16, NULL, (float *)y, NULL) == MNB_ERR_NULL);
+    CHECK(mnb_quantize_act_i8(x, 4, 100, 32, MNB_F16, (int8_t *)w, (float *)y, NULL) == MNB_ERR_SHAPE);
+    CHECK(mnb_quantize_act_i8(x, 4, 128, 32, MNB_F16, (int8_t *)w + 4, (float *)y, NULL) == MNB_ERR_ALIGN);
 }
 
 /* Writes a plan for `count` products of mixed kinds and returns its status. */
