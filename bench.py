@@ -401,34 +401,57 @@ def run_workload(cfg, steps, warmup, per_linear, torch, dev, launch_events=False
         log(f"[bench] {cfg.name}: with an event pair around each launch: avg {out['launch_ms_events'] * 1e3:.1f} us "
             f"(min {srt[0] * 1e3:.1f}, median {srt[len(srt) // 2] * 1e3:.1f}, max {srt[-1] * 1e3:.1f})")
     if per_linear:
-        def one_pass(s):
+        # prefill calls: mnb_gemm, and the split-K call (one workspace, shared
+        # by every call of the pass: they run one after another on one stream)
+        ws = None
+        if cfg.m > 1:
+            need = max(mnb.mnb_gemm_split_k_workspace_bytes(cfg.m, ld.pw, 0) for ld in base)
+            ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+
+        def one_pass(s, split=False):
             def f():
                 for ld in s:
                     if cfg.m == 1:
                         mnb.mnb_gemv(ld.x.reshape(-1), ld.pw, ld.y.reshape(-1))
+                    elif split:
+                        mnb.mnb_gemm_split_k(ld.x, ld.pw, ws, ld.y)
                     else:
                         mnb.mnb_gemm(ld.x, ld.pw, ld.y)
             return f
+
+        def graphs_of(passes):
+            # the calls captured once per replica set into a HIP graph and
+            # replayed: the device-side cost of one call per linear, without
+            # the host's per-call overhead
+            out_g = []
+            side = torch.cuda.Stream(dev)
+            side.wait_stream(torch.cuda.current_stream(dev))
+            for f in passes:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    f()
+                out_g.append(g)
+            torch.cuda.synchronize()
+            return out_g
+
         passes = [one_pass(s) for s in sets]
         pl_steps = max(3, steps // 4)
         out["per_linear_ms"], _ = time_steps(passes, pl_steps, min(warmup, 3), torch)
-        # the same calls captured once per replica set into a HIP graph and
-        # replayed: the device-side cost of one call per linear, without the
-        # host's per-call overhead
-        graphs = []
-        side = torch.cuda.Stream(dev)
-        side.wait_stream(torch.cuda.current_stream(dev))
-        for f in passes:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=side):
-                f()
-            graphs.append(g)
-        torch.cuda.synchronize()
+        graphs = graphs_of(passes)
         out["per_linear_graph_ms"], _ = time_steps([g.replay for g in graphs], max(pl_steps, 10),
                                                    max(3, min(warmup, 10)), torch)
         del graphs
         log(f"[bench] {cfg.name}: per-linear {out['per_linear_ms'] * 1e3:.1f} us/step issued from the host, "
             f"{out['per_linear_graph_ms'] * 1e3:.1f} us/step replayed from a graph")
+        if cfg.m > 1:
+            split_passes = [one_pass(s, True) for s in sets]
+            graphs = graphs_of(split_passes)
+            out["per_linear_split_graph_ms"], _ = time_steps([g.replay for g in graphs], max(pl_steps, 10),
+                                                             max(3, min(warmup, 10)), torch)
+            del graphs
+            log(f"[bench] {cfg.name}: per-linear split-K {out['per_linear_split_graph_ms'] * 1e3:.1f} us/step "
+                f"replayed from a graph")
+        del ws
     del plans, sets, base
     torch.cuda.empty_cache()
     return out
@@ -466,6 +489,9 @@ def leg_record(cfg, res, kernel):
                              "host_issued": rate(res["per_linear_ms"]),
                              "graph_ms_per_step": round(res["per_linear_graph_ms"], 5),
                              "graph": rate(res["per_linear_graph_ms"])}
+        if "per_linear_split_graph_ms" in res:
+            rec["per_linear"]["split_k_graph_ms_per_step"] = round(res["per_linear_split_graph_ms"], 5)
+            rec["per_linear"]["split_k_graph"] = rate(res["per_linear_split_graph_ms"])
     return rec
 
 

@@ -16,6 +16,8 @@ from .mnb import (  # noqa: F401
     mnb_gemm,
     mnb_gemm_i8,
     mnb_gemm_i8_workspace_bytes,
+    mnb_gemm_split_k,
+    mnb_gemm_split_k_workspace_bytes,
     mnb_gemm_grouped,
     mnb_gemv,
     mnb_pack,

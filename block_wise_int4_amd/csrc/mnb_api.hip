@@ -164,6 +164,52 @@ int mnb_gemm_i8(const void *x, const void *packed, void *y, void *workspace, siz
     return hip_status(launch_gemm_i8(p, dtype, workspace, as_stream(stream)));
 }
 
+namespace {
+// The K split a split-K call uses: 0 asks for the library's choice; the
+// split applies to the matrix-core kernel only (float16, M >= 2) and never
+// exceeds the product's K-tiles.
+int effective_ksplit(const Problem &p, int kind, int variant, int ksplit) {
+    if (kind != kKindGemm) return 1;
+    int s = ksplit == 0 ? gemm_auto_ksplit(p, variant) : ksplit;
+    if (s > p.kg) s = (int)p.kg;
+    return s < 1 ? 1 : s;
+}
+}  // namespace
+
+size_t mnb_gemm_split_k_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits, int block_size, int dtype,
+                                        int ksplit) {
+    if (ksplit < 0 || ksplit > MNB_MAX_KSPLIT) return 0;
+    Problem p;
+    int kind = 0, variant = 0;
+    // shape checks only: stand-in pointers, never dereferenced
+    static const uint8_t probe[16] __attribute__((aligned(16))) = {0};
+    if (prepare_product(probe, probe, probe, M, N, K, bits, block_size, dtype, &p, &kind, &variant) != MNB_OK)
+        return 0;
+    return (size_t)gemm_part_bytes(p, effective_ksplit(p, kind, variant, ksplit));
+}
+
+int mnb_gemm_split_k(const void *x, const void *packed, void *y, void *workspace, size_t workspace_bytes,
+                     int64_t M, int64_t N, int64_t K, int bits, int block_size, int dtype, int ksplit,
+                     void *stream) {
+    if (ksplit < 0 || ksplit > MNB_MAX_KSPLIT) return MNB_ERR_INVALID;
+    Problem p;
+    int kind = 0, variant = 0;
+    int st = prepare_product(x, packed, y, M, N, K, bits, block_size, dtype, &p, &kind, &variant);
+    if (st) return st;
+    if (kind != kKindGemm) return hip_status(launch_gemv(p, dtype, variant, as_stream(stream)));
+    p.ksplit = effective_ksplit(p, kind, variant, ksplit);
+    if (p.ksplit > 1) {
+        const int64_t need = gemm_part_bytes(p, p.ksplit);
+        if (!workspace) return MNB_ERR_NULL;
+        if (!aligned16(workspace)) return MNB_ERR_ALIGN;
+        if (workspace_bytes < (size_t)need) return MNB_ERR_INVALID;
+        if ((int64_t)p.tiles_m * p.tiles_n * p.ksplit > 0x7FFFFFFFLL || (p.m * p.n + 1023) / 1024 > 0x7FFFFFFFLL)
+            return MNB_ERR_SHAPE;
+        p.part = static_cast<float *>(workspace);
+    }
+    return hip_status(launch_gemm(p, variant, as_stream(stream)));
+}
+
 int mnb_embed_gather(const int8_t *table, const float *row_scales, const int64_t *ids, int64_t T, int64_t V,
                      int64_t H, int dtype, void *out, void *stream) {
     if (!table || !row_scales || !ids || !out) return MNB_ERR_NULL;

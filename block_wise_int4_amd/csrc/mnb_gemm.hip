@@ -142,9 +142,20 @@ struct BRaw {
     __device__ __forceinline__ uint32_t zp(int b) const { return (z[b] >> zsh) & 15u; }
 };
 
-template <int MF, int NF, int WM, int WN, int MaxBufs>
-__device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uint8_t *lds) {
+template <int MF, int NF, int WM, int WN, int MaxBufs, bool kSplit>
+__device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg_, uint8_t *lds) {
     using C = GemmCfg<MF, NF, WM, WN, MaxBufs>;
+    // split K (kSplit): workgroup = (part, output tile); part q covers
+    // K-tiles [q * kg / S, (q + 1) * kg / S) and writes float32 partial sums
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    const int64_t S = kSplit ? p.ksplit : 1;
+    const int64_t part = kSplit ? wg_ / tiles : 0;
+    const int64_t wg = kSplit ? wg_ - part * tiles : wg_;
+    const int64_t c_begin = kSplit ? part * p.kg / S : 0;
+    const int64_t c_end = kSplit ? (part + 1) * p.kg / S : p.kg;
+    // inputs of this part end at k_end; it reads metadata groups below g_end
+    const int64_t k_end = kSplit && c_end * kTileK < p.k ? c_end * kTileK : p.k;
+    const int64_t g_end = (c_end + kMetaGroup - 1) / kMetaGroup;
     const int64_t tn = wg % p.tiles_n;
     const int64_t tm = wg / p.tiles_n;
     const int64_t m0 = tm * C::kMT;
@@ -173,7 +184,7 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     const int jk = j * kChunk;
     auto line_dst = [&](int64_t stage) {  // stage = K-tile
         const int64_t first = stage * kTileK;
-        const int64_t left = p.k - first;
+        const int64_t left = k_end - first;
         return LineDst{lds + (int)((uint32_t)stage % (uint32_t)C::kBufs) * C::kStageBytes, (uint32_t)(first * 2),
                        (int32_t)(left < kTileK ? left : 0x40000000)};
     };
@@ -249,11 +260,11 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
 #pragma unroll
         for (int b = 0; b < NF; ++b) acc[a][b] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int64_t n_stages = p.kg;
+    const int64_t n_stages = c_end - c_begin;
     // the next stage's lines must have landed; those two stages ahead may
     // still be in flight (each wave waits for its own loads, then the barrier)
     auto stage_sync = [&](int64_t stage) {
-        if (C::kBufs == 3 && stage + 2 < n_stages) {
+        if (C::kBufs == 3 && stage + 2 < c_end) {
             wait_vmem<C::kLinesPerWave>();
         } else {
             wait_vmem<0>();
@@ -269,7 +280,6 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     // float16 pair of the next slice's B operands into the free slot (slice t
     // multiplies from slot t & 1).
     h8 s0[NF], s1[NF];
-    const int64_t n_groups = (p.kg + kMetaGroup - 1) / kMetaGroup;
     // B operands: float16 pairs in the shared dequant pair form, whose masks
     // and offsets are held in registers (literal constants cannot go into
     // the three-operand form), so that masking a pair and adding the offset
@@ -346,8 +356,8 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     // (after the last K-tile Rn holds no weights; its slice is formed and never used)
     auto tile = [&](int64_t c, const BRaw<NF> &Rc, BRaw<NF> &Rn) {
         const int64_t st = c;
-        if (c % kMetaGroup == 0 && c / kMetaGroup + 1 < n_groups) issue_meta(c / kMetaGroup + 1);
-        if (c + 1 < p.kg) {
+        if (c % kMetaGroup == 0 && c / kMetaGroup + 1 < g_end) issue_meta(c / kMetaGroup + 1);
+        if (c + 1 < c_end) {
             load_codes(c + 1, Rn);
             read_meta(c + 1, Rn);
         }
@@ -369,17 +379,20 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     // metadata, codes and lines of the first K-tile all in flight at once;
     // the metadata is issued first (pinned by a scheduling barrier), since
     // the wait below counts the loads issued after it
+    // (a part that starts inside a metadata group also needs the next group
+    // before its first group boundary, where the loop issues the one after)
     const bool two = C::kBufs == 3 && n_stages > 1;
-    issue_meta(0);
+    issue_meta(c_begin / kMetaGroup);
+    if (c_begin % kMetaGroup != 0 && c_begin / kMetaGroup + 1 < g_end) issue_meta(c_begin / kMetaGroup + 1);
     __builtin_amdgcn_sched_barrier(0);
-    load_codes(0, R0);
-    issue_a(0);
-    if (two) issue_a(1);
+    load_codes(c_begin, R0);
+    issue_a(c_begin);
+    if (two) issue_a(c_begin + 1);
     // tile group 0's metadata has landed once at most the codes and the
     // lines are pending
     if (two) wait_vmem<NF + 2 * C::kLinesPerWave>();
     else wait_vmem<NF + C::kLinesPerWave>();
-    read_meta(0, R0);
+    read_meta(c_begin, R0);
     dequant_t(R0, 0, s0);
     if (two) {
         wait_vmem<C::kLinesPerWave>();
@@ -388,12 +401,12 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     }
     __syncthreads();
 
-    int64_t c = 0;
-    for (; c + 2 <= p.kg; c += 2) {
+    int64_t c = c_begin;
+    for (; c + 2 <= c_end; c += 2) {
         tile(c, R0, R1);
         tile(c + 1, R1, R0);
     }
-    if (c < p.kg) tile(c, R0, R1);
+    if (c < c_end) tile(c, R0, R1);
 
     // ---- epilogue: lane holds rows j*4 + i, column r of each fragment ------
     // (every wave is past the last barrier, so the stage buffers and the
@@ -401,6 +414,23 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     _Float16 *y = static_cast<_Float16 *>(p.y);
     const int64_t n_base = (g0 + wn * NF) * kTileRows;
     const int64_t m_base = m0 + wm * MF * 16;
+    if (kSplit) {  // float32 partial sums of this K part; a second launch adds the parts
+        float *dst = p.part + part * p.m * p.n;
+#pragma unroll
+        for (int b = 0; b < NF; ++b) {
+            const int64_t n = n_base + b * kTileRows + r;
+            if (n >= p.n) continue;
+#pragma unroll
+            for (int a = 0; a < MF; ++a) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t m = m_base + a * 16 + j * 4 + i;
+                    if (m < p.m) dst[m * p.n + n] = acc[a][b][i];
+                }
+            }
+        }
+        return;
+    }
     if (p.n % 8 == 0) {
         uint8_t *ob = lds + wave * C::kOutWaveBytes;
 #pragma unroll
@@ -442,10 +472,10 @@ __device__ __forceinline__ void gemm_workgroup(const Problem &p, int64_t wg, uin
     }
 }
 
-template <int MF, int NF, int WM, int WN, int MaxBufs>
+template <int MF, int NF, int WM, int WN, int MaxBufs, bool kSplit>
 __global__ __launch_bounds__(64 * WM *WN) void gemm_kernel(Problem p) {
     __shared__ __align__(1024) uint8_t lds[GemmCfg<MF, NF, WM, WN, MaxBufs>::kLdsBytes];
-    gemm_workgroup<MF, NF, WM, WN, MaxBufs>(p, xcd_logical_wg(blockIdx.x, gridDim.x), lds);
+    gemm_workgroup<MF, NF, WM, WN, MaxBufs, kSplit>(p, xcd_logical_wg(blockIdx.x, gridDim.x), lds);
 }
 
 // The product of entries[first, last) (tiles in increasing wg_begin order)
@@ -478,7 +508,33 @@ __global__ __launch_bounds__(64 * WM *WN) void gemm_grouped_kernel(const Problem
     if (wg >= split.begin[x + 1]) return;
     const int i = find_gemm_problem(entries, split.first[x], split.first[x + 1], wg);
     const Problem p = entries[i];
-    gemm_workgroup<MF, NF, WM, WN, MaxBufs>(p, wg - p.wg_begin, lds);
+    gemm_workgroup<MF, NF, WM, WN, MaxBufs, false>(p, wg - p.wg_begin, lds);
+}
+
+// Split-K: y = float16(part[0] + part[1] + ... + part[S - 1]), the parts
+// added in that fixed order, 4 outputs per thread.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ part, int S, int64_t mn,
+                                                            _Float16 *__restrict__ y) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= mn) return;
+    if (mn % 4 == 0) {
+        float4 v = *reinterpret_cast<const float4 *>(part + i);
+        for (int s = 1; s < S; ++s) {
+            const float4 w = *reinterpret_cast<const float4 *>(part + s * mn + i);
+            v.x += w.x;
+            v.y += w.y;
+            v.z += w.z;
+            v.w += w.w;
+        }
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        *reinterpret_cast<h4 *>(y + i) = h4{(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+        return;
+    }
+    for (int64_t q = i; q < i + 4 && q < mn; ++q) {
+        float v = part[q];
+        for (int s = 1; s < S; ++s) v += part[s * mn + q];
+        y[q] = (_Float16)v;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -529,15 +585,63 @@ void gemm_tiles(const Problem &p, int variant, int32_t *tiles_m, int32_t *tiles_
     X(3, 13, 2, 1, 8, 3)                              \
     X(4, 12, 2, 1, 8, 3)
 
+// Workgroups one CU holds at once, per variant (LDS-bound).
+static int wgs_per_cu(int variant) { return variant <= 2 ? 2 : 1; }
+constexpr int kCus = 256;
+constexpr int kMaxKSplit = 16;
+
+// Choice of the K split, from a cost model fitted to single-product timings
+// on MI355X: a workgroup takes (K-tiles + 2) steps (its start and end cost
+// about two K-tiles), a step takes t0 with the chip lightly loaded and up to
+// 1.6 t0 with every workgroup slot busy, workgroups beyond one round of slots
+// run in further rounds, and a split adds its float32 partial sums (written
+// once, read once) at about 6 TB/s plus about 6 us for the partial-sum
+// epilogue and the second launch (measured: the adding kernel alone takes 3
+// to 4 us). The split with the lowest estimate wins; a larger split must be
+// at least 3% better.
+int gemm_auto_ksplit(const Problem &p, int variant) {
+    const double t0 = variant <= 2 ? 1.2 : 2.0;  // microseconds per K-tile step
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    const int64_t slots = (int64_t)kCus * wgs_per_cu(variant);
+    const int64_t top = p.kg < kMaxKSplit ? p.kg : kMaxKSplit;
+    double best_t = 0.0;
+    int best = 1;
+    for (int64_t s = 1; s <= top; ++s) {
+        const int64_t wgs = tiles * s;
+        const int64_t rounds = (wgs + slots - 1) / slots;
+        const double fill = wgs < slots ? (double)wgs / (double)slots : 1.0;
+        const int64_t steps = (p.kg + s - 1) / s + 2;
+        double t = (double)rounds * (double)steps * t0 * (1.0 + 0.6 * fill);
+        if (s > 1) t += (2.0 * (double)s + 0.5) * (double)p.m * (double)p.n * 4.0 / 6.0e6 + 6.0;
+        if (s == 1 || t < 0.97 * best_t) {
+            best_t = t;
+            best = (int)s;
+        }
+    }
+    return best;
+}
+
+int64_t gemm_part_bytes(const Problem &p, int ksplit) {
+    return ksplit > 1 ? align_up((int64_t)ksplit * p.m * p.n * 4, kAlign) : 0;
+}
+
 hipError_t launch_gemm(const Problem &p, int variant, hipStream_t st) {
-    const unsigned grid = (unsigned)((int64_t)p.tiles_m * p.tiles_n);
+    const unsigned grid = (unsigned)((int64_t)p.tiles_m * p.tiles_n * (p.ksplit > 1 ? p.ksplit : 1));
     switch (variant) {
-#define X(V, MF, NF, WM, WN, B) \
-    case V: gemm_kernel<MF, NF, WM, WN, B><<<grid, 64 * WM * WN, 0, st>>>(p); break;
+#define X(V, MF, NF, WM, WN, B)                                                           \
+    case V:                                                                                \
+        if (p.ksplit > 1) gemm_kernel<MF, NF, WM, WN, B, true><<<grid, 64 * WM * WN, 0, st>>>(p); \
+        else gemm_kernel<MF, NF, WM, WN, B, false><<<grid, 64 * WM * WN, 0, st>>>(p);             \
+        break;
         MNB_GEMM_VARIANTS(X)
 #undef X
     default: return hipErrorInvalidValue;
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.ksplit <= 1) return e;
+    const int64_t mn = p.m * p.n;
+    splitk_reduce_kernel<<<(unsigned)((mn + 1023) / 1024), 256, 0, st>>>(p.part, p.ksplit, mn,
+                                                                         static_cast<_Float16 *>(p.y));
     return hipGetLastError();
 }
 

@@ -27,7 +27,8 @@ struct Problem {
     int32_t bs, nbt;
     int32_t variant;         // kernel variant index (see mnb_gemm.hip / mnb_gemv.hip)
     int32_t tiles_m, tiles_n;
-    int32_t pad_;
+    int32_t ksplit;          // prefill kernel: K parts per output tile (1 = none)
+    float *part;             // with ksplit > 1: float32 partial sums [ksplit][m][n]
 };
 
 // Kernel classes a plan can launch.
@@ -93,6 +94,7 @@ inline Problem make_problem(const void *x, const void *packed, void *y, int64_t 
     p.zp_off = L.zp_off;
     p.bs = bs;
     p.nbt = L.nbt;
+    p.ksplit = 1;
     return p;
 }
 
@@ -138,6 +140,12 @@ hipError_t launch_gemm_i8(const Problem &p, int dtype, void *workspace, hipStrea
 // MFMA kernel: fp16 with M >= 2.
 int gemm_variant(int64_t m);
 void gemm_tiles(const Problem &p, int variant, int32_t *tiles_m, int32_t *tiles_n);
+// K parts a single product splits into (when a caller workspace allows it):
+// enough to give the chip several workgroups per CU, each part at least two
+// K-tiles long.
+int gemm_auto_ksplit(const Problem &p, int variant);
+// Bytes of float32 partial sums a product split into `ksplit` parts needs.
+int64_t gemm_part_bytes(const Problem &p, int ksplit);
 hipError_t launch_gemm(const Problem &p, int variant, hipStream_t st);
 hipError_t launch_gemm_grouped(const Problem *dev_entries, int count, const XcdSplit &split, int variant,
                                hipStream_t st);

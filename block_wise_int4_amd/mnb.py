@@ -56,6 +56,8 @@ _SIGNATURES = {
     "mnb_gemv_argmax_noalloc": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
     "mnb_embed_gather": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _vp]),
     "mnb_gemm": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp]),
+    "mnb_gemm_split_k_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _int, _int]),
+    "mnb_gemm_split_k": (_int, [_vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _int, _int, _int, _int, _vp]),
     "mnb_gemm_i8_workspace_bytes": (_sz, [_i64, _i64, _int]),
     "mnb_quantize_act_i8": (_int, [_vp, _i64, _i64, _int, _int, _vp, _vp, _vp]),
     "mnb_gemm_i8": (_int, [_vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _int, _int, _int, _vp]),
@@ -385,6 +387,45 @@ def mnb_gemm_grouped(plan):
     _check("mnb_gemm_grouped", lib().mnb_gemm_grouped(
         ctypes.c_void_p(plan.host.data_ptr()), _dev(plan.device, "plan_device"), _stream(plan.device.device)))
     return plan.outputs
+
+
+MAX_KSPLIT = 16
+
+
+def mnb_gemm_split_k_workspace_bytes(M, pw, ksplit=0):
+    """Workspace bytes mnb_gemm_split_k needs for M rows times this weight."""
+    return lib().mnb_gemm_split_k_workspace_bytes(M, pw.N, pw.K, pw.bits, pw.block_size, dtype_code(pw.dtype),
+                                                  ksplit)
+
+
+def split_k_workspace(M, pw, ksplit=0, device=None):
+    """A workspace for mnb_gemm_split_k (None when the call splits nothing)."""
+    nbytes = mnb_gemm_split_k_workspace_bytes(M, pw, ksplit)
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device or pw.packed.device)
+
+
+def mnb_gemm_split_k(x, pw, workspace=None, y=None, ksplit=0):
+    """Y = X @ dequant(W)^T with K split over workgroups (float32 partial
+    sums in `workspace`, added in a fixed order by a second launch)."""
+    _check_x(x, pw)
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M = x.shape[0]
+    if workspace is None:
+        workspace = split_k_workspace(M, pw, ksplit, x.device)
+    if workspace is not None and workspace.device != x.device:
+        raise ValueError(f"workspace is on {workspace.device}, not {x.device}")
+    if y is None:
+        y = torch.empty((M, pw.N), dtype=pw.dtype, device=x.device)
+    _check_buf(y, "y", pw.dtype, M * pw.N, x.device)
+    ws_ptr = None if workspace is None else _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("mnb_gemm_split_k", lib().mnb_gemm_split_k(
+        _dev(x, "x"), _dev(pw.packed, "packed"), _dev(y, "y"), ws_ptr, ws_bytes, M, pw.N, pw.K, pw.bits,
+        pw.block_size, dtype_code(pw.dtype), ksplit, _stream(x.device)))
+    return y
 
 
 def mnb_gemm_i8_workspace_bytes(M, K, block_size):

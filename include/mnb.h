@@ -239,6 +239,39 @@ int mnb_gemm(const void *x, const void *packed, void *y,
              int64_t M, int64_t N, int64_t K, int bits, int block_size, int dtype, void *stream);
 
 /*
+ * Split-K form of mnb_gemm, for a product too small to fill the GPU by its
+ * output tiles alone (a single linear of a prefill). Same product, same
+ * arguments as mnb_gemm, plus a caller workspace: the matrix-core kernel
+ * (float16, M >= 2) splits K into `ksplit` contiguous ranges of whole
+ * 128-input tiles, each workgroup writes the float32 partial sums of one
+ * range into the workspace, and a second launch adds the ranges in a fixed
+ * order (range 0 first) and rounds once to float16. The result is
+ * deterministic (the same bits on every call with the same arguments); it
+ * can differ from mnb_gemm's in the last bit, since the float32 sums are
+ * grouped differently. Other calls (M = 1, float32) run exactly as
+ * mnb_gemm and ignore the workspace.
+ *
+ * ksplit: 0 = the library's choice (enough ranges to give every compute
+ * unit work, each range at least two tiles long, none when the output
+ * tiles already fill the GPU); 1 = no split (one launch, as mnb_gemm);
+ * 2..MNB_MAX_KSPLIT = that many ranges, capped at the number of 128-input
+ * tiles. Anything else: MNB_ERR_INVALID.
+ *
+ * mnb_gemm_split_k_workspace_bytes: the workspace bytes a call with these
+ * arguments needs (0 when it splits nothing, or when the arguments are
+ * invalid). workspace: device, 16-byte aligned, at least that many bytes
+ * (MNB_ERR_INVALID if workspace_bytes is smaller; may be NULL when 0 is
+ * needed); its contents are overwritten, and calls that may overlap must
+ * not share it.
+ */
+#define MNB_MAX_KSPLIT 16
+size_t mnb_gemm_split_k_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits, int block_size, int dtype,
+                                        int ksplit);
+int mnb_gemm_split_k(const void *x, const void *packed, void *y, void *workspace, size_t workspace_bytes,
+                     int64_t M, int64_t N, int64_t K, int bits, int block_size, int dtype, int ksplit,
+                     void *stream);
+
+/*
  * Int8 compute mode. The published int4 exports set an accuracy level of 4
  * ("Qwen3-ASR-0.6B ONNX for the browser", section "Pick a variant";
  * "sherpa-onnx STT int4", section "whisper-small"), read here as

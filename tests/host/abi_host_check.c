@@ -90,6 +90,27 @@ static void check_invalid_calls(void) {
                            NULL) == MNB_ERR_SHAPE);
     CHECK(mnb_embed_gather((const int8_t *)w, (const float *)x, (const int64_t *)ws, 0, 100, 16, MNB_F16, y,
                            NULL) == MNB_OK);
+    /* split-K */
+    CHECK(mnb_gemm_split_k_workspace_bytes(1, 2048, 2048, 4, 32, MNB_F16, 0) == 0);
+    CHECK(mnb_gemm_split_k_workspace_bytes(410, 2048, 2048, 4, 32, MNB_F32, 0) == 0);
+    CHECK(mnb_gemm_split_k_workspace_bytes(410, 2048, 2048, 4, 32, MNB_F16, 1) == 0);
+    CHECK(mnb_gemm_split_k_workspace_bytes(410, 2048, 2048, 4, 32, MNB_F16, 4) >= (size_t)4 * 410 * 2048 * 4);
+    CHECK(mnb_gemm_split_k_workspace_bytes(410, 2048, 2048, 4, 32, MNB_F16, 0) > 0);
+    CHECK(mnb_gemm_split_k_workspace_bytes(410, 2048, 2048, 4, 32, MNB_F16, MNB_MAX_KSPLIT + 1) == 0);
+    CHECK(mnb_gemm_split_k_workspace_bytes(410, 2048, 2048, 4, 32, MNB_F16, -1) == 0);
+    CHECK(mnb_gemm_split_k_workspace_bytes(410, 2048, 100, 4, 32, MNB_F16, 0) == 0);
+    /* a split never exceeds the K-tiles: 2 tiles, 16 asked */
+    CHECK(mnb_gemm_split_k_workspace_bytes(64, 64, 256, 4, 32, MNB_F16, 16) ==
+          mnb_gemm_split_k_workspace_bytes(64, 64, 256, 4, 32, MNB_F16, 2));
+    {
+        const size_t need = mnb_gemm_split_k_workspace_bytes(64, 64, 2048, 4, 32, MNB_F16, 4);
+        CHECK(mnb_gemm_split_k(x, w, y, NULL, need, 64, 64, 2048, 4, 32, MNB_F16, 4, NULL) == MNB_ERR_NULL);
+        CHECK(mnb_gemm_split_k(x, w, y, ws, need - 1, 64, 64, 2048, 4, 32, MNB_F16, 4, NULL) == MNB_ERR_INVALID);
+        CHECK(mnb_gemm_split_k(x, w, y, (char *)ws + 4, need, 64, 64, 2048, 4, 32, MNB_F16, 4, NULL) ==
+              MNB_ERR_ALIGN);
+        CHECK(mnb_gemm_split_k(x, w, y, ws, need, 64, 64, 2048, 4, 32, MNB_F16, 17, NULL) == MNB_ERR_INVALID);
+        CHECK(mnb_gemm_split_k(x, w, y, ws, need, 64, 64, 2000, 4, 32, MNB_F16, 4, NULL) == MNB_ERR_SHAPE);
+    }
     /* int8 compute mode */
     const size_t wsb = mnb_gemm_i8_workspace_bytes(4, 128, 32);
     CHECK(wsb >= 4 * 128 && wsb % 256 == 0);
