@@ -562,6 +562,54 @@ def run_embed_gather(cfg, steps, warmup, torch, dev, token_counts=(410, 65536)):
     return res
 
 
+def run_int8_mode(cfg, steps, warmup, torch, dev):
+    """The workload in the int8 compute mode (activations quantized per block
+    to int8, integer dot products): one mnb_gemm_i8 call per linear (two
+    launches: quantize, product), captured in a HIP graph per replica set and
+    replayed. Bytes: the step's algorithmic bytes (codes, scales, zero
+    points, activations and outputs)."""
+    from block_wise_int4_amd import mnb, workload
+
+    base = workload.build_config(cfg, dev).linears
+    algo = workload.algorithmic_bytes(cfg)
+    weight_bytes = sum(ld.pw.packed.numel() for ld in base)
+    replicas = max(1, math.ceil(1.1e9 / weight_bytes))
+    sets = [base] + [workload.replicate(cfg, base) for _ in range(replicas - 1)]
+    need = max(mnb.mnb_gemm_i8_workspace_bytes(cfg.m, ld.pw.K, ld.pw.block_size) for ld in base)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def one_pass(s):
+        def f():
+            for ld in s:
+                mnb.mnb_gemm_i8(ld.x.reshape(cfg.m, -1), ld.pw, ws, ld.y.reshape(cfg.m, -1))
+        return f
+    passes = [one_pass(s) for s in sets]
+    for f in passes:
+        f()
+    torch.cuda.synchronize()
+    graphs = []
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    for f in passes:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            f()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    ms, _ = time_steps([g.replay for g in graphs], max(10, steps // 4), max(3, min(warmup, 10)), torch)
+    gbs = algo / (ms * 1e-3) / 1e9
+    log(f"[bench] {cfg.name} int8 compute mode: {ms * 1e3:.1f} us/step from a graph ({gbs:.0f} GB/s)")
+    del graphs, sets, base, ws
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "mode": "int8 activations (per-block symmetric), integer dot products",
+            "schedule": "per-linear mnb_gemm_i8 (quantize + product launches), replayed from a graph",
+            "launches_per_step": 2 * len(cfg.linears), "replicas": replicas,
+            "ms_per_step": round(ms, 5), "value": round(gbs, 2), "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": algo,
+                         "timing": "graph replay time per step (all launches of the step)"}}
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -645,7 +693,8 @@ def main():
                     help="further workloads timed as legs of the line (comma-separated indices; '' = none)")
     ap.add_argument("--no-per-linear", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-next", action="store_true", help="skip the LM-head argmax and embedding-gather lines")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the LM-head argmax, embedding-gather and int8-mode lines")
     ap.add_argument("--launch-events", action="store_true",
                     help="also time each launch between its own event pair (diagnostic; logged, not reported)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per workload")
@@ -744,6 +793,9 @@ def main():
     if any(l.proj == "lm_head" for l in cfg.linears) and not args.no_next:
         result["lm_head_argmax"] = run_lm_head_argmax(cfg, args.steps, args.warmup, torch, dev)
         result["embedding_gather"] = run_embed_gather(cfg, args.steps, args.warmup, torch, dev)
+
+    if not args.no_next:
+        result["int8_mode"] = run_int8_mode(cfg, args.steps, args.warmup, torch, dev)
 
     if args.prefill_config >= 0:
         pcfg = configs.CONFIGS[args.prefill_config]

@@ -94,3 +94,35 @@ def test_argmax_full_size_lm_head():
     w, x = synth.linear_inputs(cfg, lin)
     pw, parts = _packed(w, cfg.block_size, np.float16)
     _check(x, pw, parts, cfg.block_size, np.float16)
+
+
+def test_argmax_graph_replays():
+    """The fused call captured in a HIP graph and replayed with new inputs
+    copied into the captured buffer: every replay's index matches the eager
+    product's argmax (both launches captured; nothing needs clearing between
+    replays: every slot the finishing launch reads is written first)."""
+    n, k, bs = 151936, 1024, 32
+    w, _ = synth.random_case(600, 1, n, k, "f16")
+    pw, parts = _packed(w, bs, np.float16)
+    ws = mnb.argmax_workspace(DEV)
+    xin = torch.empty(k, dtype=torch.float16, device=DEV)
+    idx = torch.empty(1, dtype=torch.int64, device=DEV)
+    _, x0 = synth.random_case(601, 1, n, k, "f16")
+    xin.copy_(torch.from_numpy(x0.reshape(-1)))
+    mnb.mnb_gemv_argmax(xin, pw, ws, index=idx)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        mnb.mnb_gemv_argmax(xin, pw, ws, index=idx)
+    torch.cuda.synchronize()
+    for seed in range(4):
+        _, x = synth.random_case(610 + seed, 1, n, k, "f16")
+        xin.copy_(torch.from_numpy(x.reshape(-1)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        y = mnb.mnb_gemv(xin, pw)
+        torch.cuda.synchronize()
+        assert int(idx.item()) == int(np.argmax(y.float().cpu().numpy())), f"replay {seed}"
