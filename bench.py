@@ -563,11 +563,12 @@ def run_embed_gather(cfg, steps, warmup, torch, dev, token_counts=(410, 65536)):
 
 
 def run_int8_mode(cfg, steps, warmup, torch, dev):
-    """The workload in the int8 compute mode (activations quantized per block
-    to int8, integer dot products): one mnb_gemm_i8 call per linear (two
-    launches: quantize, product), captured in a HIP graph per replica set and
-    replayed. Bytes: the step's algorithmic bytes (codes, scales, zero
-    points, activations and outputs)."""
+    """The decode workload in the int8 compute mode (activations quantized
+    per block to int8 inside the kernel, integer dot products): the whole
+    step as one grouped launch (mnb_plan_grouped_i8), rotating over replicas
+    past the last-level cache; and, for context, one mnb_gemm_i8 call per
+    linear replayed from a HIP graph. Bytes: the step's algorithmic bytes
+    (codes, scales, zero points, activations and outputs)."""
     from block_wise_int4_amd import mnb, workload
 
     base = workload.build_config(cfg, dev).linears
@@ -575,13 +576,21 @@ def run_int8_mode(cfg, steps, warmup, torch, dev):
     weight_bytes = sum(ld.pw.packed.numel() for ld in base)
     replicas = max(1, math.ceil(1.1e9 / weight_bytes))
     sets = [base] + [workload.replicate(cfg, base) for _ in range(replicas - 1)]
-    need = max(mnb.mnb_gemm_i8_workspace_bytes(cfg.m, ld.pw.K, ld.pw.block_size) for ld in base)
-    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    dt = torch.float16 if cfg.dtype == "f16" else torch.float32
+    plans = [mnb.mnb_plan_grouped([(ld.x.reshape(-1), ld.pw, ld.y) for ld in s], cfg.block_size, dt, int8=True)
+             for s in sets]
+    launches = mnb.mnb_plan_launches(plans[0])
+    fns = [lambda p=p: mnb.mnb_gemm_grouped(p) for p in plans]
+    first_ms, _ = time_steps(fns[:1], 1, 0, torch)
+    ms, _ = time_steps(fns, steps, max(warmup - 1, 0), torch)
+    gbs = algo / (ms * 1e-3) / 1e9
+    log(f"[bench] {cfg.name} int8 compute mode: grouped {ms * 1e3:.1f} us/step ({gbs:.0f} GB/s, "
+        f"{launches} launch per step)")
 
     def one_pass(s):
         def f():
             for ld in s:
-                mnb.mnb_gemm_i8(ld.x.reshape(cfg.m, -1), ld.pw, ws, ld.y.reshape(cfg.m, -1))
+                mnb.mnb_gemm_i8(ld.x.reshape(cfg.m, -1), ld.pw, None, ld.y.reshape(cfg.m, -1))
         return f
     passes = [one_pass(s) for s in sets]
     for f in passes:
@@ -596,18 +605,22 @@ def run_int8_mode(cfg, steps, warmup, torch, dev):
             f()
         graphs.append(g)
     torch.cuda.synchronize()
-    ms, _ = time_steps([g.replay for g in graphs], max(10, steps // 4), max(3, min(warmup, 10)), torch)
-    gbs = algo / (ms * 1e-3) / 1e9
-    log(f"[bench] {cfg.name} int8 compute mode: {ms * 1e3:.1f} us/step from a graph ({gbs:.0f} GB/s)")
-    del graphs, sets, base, ws
+    pl_ms, _ = time_steps([g.replay for g in graphs], max(10, steps // 4), max(3, min(warmup, 10)), torch)
+    log(f"[bench] {cfg.name} int8 compute mode: per-linear {pl_ms * 1e3:.1f} us/step from a graph")
+    del graphs, plans, sets, base
     torch.cuda.empty_cache()
-    return {"workload": cfg.name, "mode": "int8 activations (per-block symmetric), integer dot products",
-            "schedule": "per-linear mnb_gemm_i8 (quantize + product launches), replayed from a graph",
-            "launches_per_step": 2 * len(cfg.linears), "replicas": replicas,
-            "ms_per_step": round(ms, 5), "value": round(gbs, 2), "unit": "GB/s",
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": algo,
-                         "timing": "graph replay time per step (all launches of the step)"}}
+    roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "decode_i8_grouped_kernel",
+            "launch_us": round(ms * 1e3, 2), "algorithmic_bytes_per_launch": algo}
+    if launches == 1:
+        roof["launch_timing"] = "timed region / steps (one launch per step, back to back)"
+    return {"workload": cfg.name, "mode": "int8 activations (per-block symmetric, quantized in LDS), "
+                                          "integer dot products",
+            "schedule": "grouped", "launches_per_step": launches, "replicas": replicas, "steps": steps,
+            "ms_per_step": round(ms, 5), "first_launch_us": round(first_ms * 1e3, 2),
+            "value": round(gbs, 2), "unit": "GB/s", "roofline": roof,
+            "per_linear": {"unit": "GB/s", "graph_ms_per_step": round(pl_ms, 5),
+                           "graph": round(algo / (pl_ms * 1e-3) / 1e9, 2)}}
 
 
 def cpu_model():

@@ -135,7 +135,7 @@ int mnb_gemm(const void *x, const void *packed, void *y, int64_t M, int64_t N, i
 
 size_t mnb_gemm_i8_workspace_bytes(int64_t M, int64_t K, int block_size) {
     if (check_format(1, K, 4, block_size, MNB_F32) != MNB_OK) return 0;
-    if (M <= 0 || M > MNB_MAX_ROWS) return 0;
+    if (M <= 1 || M > MNB_MAX_ROWS) return 0;  // M = 1 quantizes in LDS and needs none
     return (size_t)a8_workspace_bytes(M, K, block_size);
 }
 
@@ -153,11 +153,17 @@ int mnb_quantize_act_i8(const void *x, int64_t M, int64_t K, int block_size, int
 
 int mnb_gemm_i8(const void *x, const void *packed, void *y, void *workspace, size_t workspace_bytes, int64_t M,
                 int64_t N, int64_t K, int bits, int block_size, int dtype, void *stream) {
-    if (!x || !packed || !y || !workspace) return MNB_ERR_NULL;
+    if (!x || !packed || !y) return MNB_ERR_NULL;
     int st = check_format(N, K, bits, block_size, dtype);
     if (st) return st;
     if (M <= 0 || M > MNB_MAX_ROWS) return MNB_ERR_SHAPE;
-    if (!aligned16(x) || !aligned16(packed) || !aligned16(y) || !aligned16(workspace)) return MNB_ERR_ALIGN;
+    if (!aligned16(x) || !aligned16(packed) || !aligned16(y)) return MNB_ERR_ALIGN;
+    if (M == 1) {
+        const Problem p = make_problem(x, packed, y, 1, N, K, block_size, dtype_bytes(dtype));
+        return hip_status(launch_gemv_i8(p, dtype, as_stream(stream)));
+    }
+    if (!workspace) return MNB_ERR_NULL;
+    if (!aligned16(workspace)) return MNB_ERR_ALIGN;
     if (workspace_bytes < (size_t)a8_workspace_bytes(M, K, block_size)) return MNB_ERR_INVALID;
     const Problem p = make_problem(x, packed, y, M, N, K, block_size, dtype_bytes(dtype));
     if ((M * (K / 8) + 255) / 256 > 0x7FFFFFFFLL || gemm_i8_workgroups(p) > 0x7FFFFFFFLL) return MNB_ERR_SHAPE;
@@ -262,8 +268,9 @@ size_t mnb_plan_bytes(int count) {
            sizeof(GemvWg) * (size_t)kGemvMaxWgs * kGemvMaxLaunches;
 }
 
-int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block_size, int dtype, void *plan,
-                     size_t plan_bytes) {
+namespace {
+int plan_grouped(const mnb_problem *problems, int count, int bits, int block_size, int dtype, bool int8, void *plan,
+                 size_t plan_bytes) {
     if (!problems || !plan) return MNB_ERR_NULL;
     const size_t need = mnb_plan_bytes(count);
     if (need == 0 || plan_bytes < need) return MNB_ERR_PLAN;
@@ -286,6 +293,11 @@ int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block
         const mnb_problem &q = problems[i];
         st = prepare_product(q.x, q.packed, q.y, q.M, q.N, q.K, bits, block_size, dtype, &tmp[i], &kinds[i],
                              &variants[i]);
+        if (st == MNB_OK && int8) {  // the int8 mode takes decode products: one kernel, variant = dtype
+            if (q.M != 1) st = MNB_ERR_SHAPE;
+            kinds[i] = kKindGemvI8;
+            variants[i] = dtype == MNB_F16 ? 0 : 1;
+        }
     }
     if (st == MNB_OK) {
         PlanHeader *hdr = static_cast<PlanHeader *>(plan);
@@ -300,7 +312,7 @@ int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block
         hdr->dtype = dtype;
         int out = 0, decode_tables = 0;
         // one launch per (kind, variant) present
-        for (int kind = kKindGemv; kind <= kKindGemm && st == MNB_OK; ++kind) {
+        for (int kind = kKindGemv; kind <= kKindGemvI8 && st == MNB_OK; ++kind) {
             for (int v = 0; v < 16 && st == MNB_OK; ++v) {
                 PlanLaunch L{};
                 L.kind = kind;
@@ -319,6 +331,7 @@ int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block
                     if (kind == kKindGemm) wgs += (int64_t)p.tiles_m * p.tiles_n;
                     else if (v >= 2) wgs += gemv_workgroups(p, v);
                     if (kind == kKindGemv && gemv_lds_bytes(p, v) > lds) lds = gemv_lds_bytes(p, v);
+                    if (kind == kKindGemvI8 && gemv_i8_lds_bytes(p) > lds) lds = gemv_i8_lds_bytes(p);
                     entries[out++] = p;
                 }
                 L.count = out - L.first;
@@ -330,7 +343,7 @@ int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block
                     }
                     wgs = gemm_xcd_schedule(entries + L.first, L.count, &L.split);
                 }
-                if (kind == kKindGemv && v < 2) {
+                if ((kind == kKindGemv && v < 2) || kind == kKindGemvI8) {
                     if (decode_tables >= kGemvMaxLaunches) {
                         st = MNB_ERR_PLAN;
                         break;
@@ -357,6 +370,17 @@ int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block
     delete[] order;
     return st;
 }
+}  // namespace
+
+int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block_size, int dtype, void *plan,
+                     size_t plan_bytes) {
+    return plan_grouped(problems, count, bits, block_size, dtype, false, plan, plan_bytes);
+}
+
+int mnb_plan_grouped_i8(const mnb_problem *problems, int count, int bits, int block_size, int dtype, void *plan,
+                        size_t plan_bytes) {
+    return plan_grouped(problems, count, bits, block_size, dtype, true, plan, plan_bytes);
+}
 
 int mnb_plan_launches(const void *plan_host) {
     if (!plan_host) return -1;
@@ -382,6 +406,11 @@ int mnb_gemm_grouped(const void *plan_host, const void *plan_device, void *strea
         hipError_t e;
         if (L.kind == kKindGemm) {
             e = launch_gemm_grouped(dev + L.first, L.count, L.split, L.variant, as_stream(stream));
+        } else if (L.kind == kKindGemvI8) {
+            const GemvWg *table = reinterpret_cast<const GemvWg *>(static_cast<const uint8_t *>(plan_device) +
+                                                                   L.sched_off);
+            e = launch_gemv_i8_grouped(dev + L.first, table, L.wgs, L.variant == 0 ? kF16 : kF32, (size_t)L.lds,
+                                       as_stream(stream));
         } else {
             const GemvWg *table = reinterpret_cast<const GemvWg *>(static_cast<const uint8_t *>(plan_device) +
                                                                    L.sched_off);

@@ -32,7 +32,7 @@ struct Problem {
 };
 
 // Kernel classes a plan can launch.
-enum Kind : int32_t { kKindGemv = 0, kKindGemm = 1 };
+enum Kind : int32_t { kKindGemv = 0, kKindGemm = 1, kKindGemvI8 = 2 };
 
 // Prefill launches: the output tiles of XCD x (blocks b with b % 8 == x)
 // are tiles [begin[x], begin[x + 1]) of the launch, and they belong to
@@ -136,6 +136,12 @@ int64_t gemm_i8_workgroups(const Problem &p);
 hipError_t launch_quantize_act(const void *x, int64_t m, int64_t k, int bs, int dtype, int8_t *qa, float *scales,
                                hipStream_t st);
 hipError_t launch_gemm_i8(const Problem &p, int dtype, void *workspace, hipStream_t st);
+// M = 1 in the int8 mode: one launch that quantizes x in LDS (single
+// products, and grouped plans through the decode schedule).
+size_t gemv_i8_lds_bytes(const Problem &p);
+hipError_t launch_gemv_i8(const Problem &p, int dtype, hipStream_t st);
+hipError_t launch_gemv_i8_grouped(const Problem *dev_entries, const GemvWg *dev_table, int64_t wgs, int dtype,
+                                  size_t lds, hipStream_t st);
 
 // MFMA kernel: fp16 with M >= 2.
 int gemm_variant(int64_t m);

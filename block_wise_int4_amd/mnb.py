@@ -63,6 +63,7 @@ _SIGNATURES = {
     "mnb_gemm_i8": (_int, [_vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _int, _int, _int, _vp]),
     "mnb_plan_bytes": (_sz, [_int]),
     "mnb_plan_grouped": (_int, [ctypes.POINTER(mnb_problem), _int, _int, _int, _int, _vp, _sz]),
+    "mnb_plan_grouped_i8": (_int, [ctypes.POINTER(mnb_problem), _int, _int, _int, _int, _vp, _sz]),
     "mnb_plan_launches": (_int, [_vp]),
     "mnb_gemm_grouped": (_int, [_vp, _vp, _vp]),
 }
@@ -343,8 +344,9 @@ class Plan:
     inputs: list             # the x tensors and packed weights (kept alive)
 
 
-def mnb_plan_grouped(problems, block_size, dtype, device=None, bits=4):
-    """problems: list of (x [M, K], PackedWeight, y [M, N] or None). Returns a Plan."""
+def mnb_plan_grouped(problems, block_size, dtype, device=None, bits=4, int8=False):
+    """problems: list of (x [M, K], PackedWeight, y [M, N] or None). Returns a Plan.
+    int8=True plans the int8 compute mode (decode products, M = 1, only)."""
     count = len(problems)
     nbytes = lib().mnb_plan_bytes(count)
     if nbytes == 0:
@@ -371,8 +373,9 @@ def mnb_plan_grouped(problems, block_size, dtype, device=None, bits=4):
         outs.append(y)
         keep.append((x, pw))
     host = torch.empty(nbytes, dtype=torch.uint8)
-    _check("mnb_plan_grouped", lib().mnb_plan_grouped(arr, count, bits, block_size, dtype_code(dtype),
-                                                      ctypes.c_void_p(host.data_ptr()), nbytes))
+    fn = "mnb_plan_grouped_i8" if int8 else "mnb_plan_grouped"
+    _check(fn, getattr(lib(), fn)(arr, count, bits, block_size, dtype_code(dtype), ctypes.c_void_p(host.data_ptr()),
+                                  nbytes))
     dev = host.to(device)
     return Plan(host, dev, outs, keep)
 
@@ -434,7 +437,10 @@ def mnb_gemm_i8_workspace_bytes(M, K, block_size):
 
 def i8_workspace(M, K, block_size, device):
     """A workspace for mnb_gemm_i8 with M rows of K inputs (reusable by calls
-    of at most that size that run one after another on one stream)."""
+    of at most that size that run one after another on one stream; None for
+    M = 1, which needs none)."""
+    if M == 1:
+        return None
     nbytes = mnb_gemm_i8_workspace_bytes(M, K, block_size)
     if nbytes == 0:
         raise ValueError(f"no int8 workspace for M={M}, K={K}, block_size={block_size}")
@@ -462,15 +468,16 @@ def mnb_gemm_i8(x, pw, workspace=None, y=None):
     if x.dim() != 2:
         raise ValueError("x must be [M, K]")
     M = x.shape[0]
-    if workspace is None:
+    if workspace is None and M > 1:
         workspace = i8_workspace(M, pw.K, pw.block_size, x.device)
-    if workspace.device != x.device:
+    if workspace is not None and workspace.device != x.device:
         raise ValueError(f"workspace is on {workspace.device}, not {x.device}")
     if y is None:
         y = torch.empty((M, pw.N), dtype=pw.dtype, device=x.device)
     _check_buf(y, "y", pw.dtype, M * pw.N, x.device)
+    ws_ptr = None if workspace is None else _dev(workspace, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("mnb_gemm_i8", lib().mnb_gemm_i8(
-        _dev(x, "x"), _dev(pw.packed, "packed"), _dev(y, "y"), _dev(workspace, "workspace"),
-        workspace.numel() * workspace.element_size(), M, pw.N, pw.K, pw.bits, pw.block_size,
-        dtype_code(pw.dtype), _stream(x.device)))
+        _dev(x, "x"), _dev(pw.packed, "packed"), _dev(y, "y"), ws_ptr, ws_bytes, M, pw.N, pw.K, pw.bits,
+        pw.block_size, dtype_code(pw.dtype), _stream(x.device)))
     return y

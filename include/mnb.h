@@ -292,11 +292,22 @@ int mnb_gemm_split_k(const void *x, const void *packed, void *y, void *workspace
  * [M][K] (8-byte aligned); scales: device float32 [M][K / block_size].
  *
  * mnb_gemm_i8: the product, any M >= 1. x, y: device row-major [M][K],
- * [M][N] dtype; packed: mnb_pack output; workspace: device, 16-byte
- * aligned, at least mnb_gemm_i8_workspace_bytes(M, K, block_size) bytes
- * (MNB_ERR_INVALID if workspace_bytes is smaller); its contents are
- * overwritten and it must not be shared by calls that may overlap. Two
- * launches on `stream` (quantize, product); nothing is allocated.
+ * [M][N] dtype; packed: mnb_pack output. M >= 2: workspace is device
+ * memory, 16-byte aligned, at least mnb_gemm_i8_workspace_bytes(M, K,
+ * block_size) bytes (MNB_ERR_INVALID if workspace_bytes is smaller); its
+ * contents are overwritten and it must not be shared by calls that may
+ * overlap; two launches on `stream` (quantize, product). M = 1 (decode):
+ * one launch whose workgroups quantize x in their own LDS, with the
+ * quantizer's arithmetic (same codes and scales); workspace is not used
+ * (may be NULL; mnb_gemm_i8_workspace_bytes returns 0). Nothing is
+ * allocated.
+ *
+ * mnb_plan_grouped_i8 (declared with the grouped plans below):
+ * mnb_plan_grouped for the int8 mode. Every problem
+ * must have M = 1 (MNB_ERR_SHAPE otherwise): the whole decode step runs as
+ * one launch of the decode schedule, each workgroup quantizing the vector
+ * of the product it is in. Run the plan with mnb_gemm_grouped; the outputs
+ * equal single mnb_gemm_i8 calls bit for bit.
  */
 size_t mnb_gemm_i8_workspace_bytes(int64_t M, int64_t K, int block_size);
 int mnb_quantize_act_i8(const void *x, int64_t M, int64_t K, int block_size, int dtype, int8_t *qa, float *scales,
@@ -326,6 +337,11 @@ size_t mnb_plan_bytes(int count);
  */
 int mnb_plan_grouped(const mnb_problem *problems, int count, int bits, int block_size, int dtype,
                      void *plan, size_t plan_bytes);
+
+/* The int8 compute mode's plan (decode products only; described with
+ * mnb_gemm_i8 above). Same arguments and plan image as mnb_plan_grouped. */
+int mnb_plan_grouped_i8(const mnb_problem *problems, int count, int bits, int block_size, int dtype,
+                        void *plan, size_t plan_bytes);
 
 /* Kernel launches mnb_gemm_grouped issues for a plan (one per kernel class
  * and tile variant present), or -1 if `plan_host` is not a valid plan. Host only. */

@@ -112,6 +112,26 @@ static void check_invalid_calls(void) {
         CHECK(mnb_gemm_split_k(x, w, y, ws, need, 64, 64, 2000, 4, 32, MNB_F16, 4, NULL) == MNB_ERR_SHAPE);
     }
     /* int8 compute mode */
+    CHECK(mnb_gemm_i8_workspace_bytes(1, 4096, 32) == 0);
+    {
+        mnb_problem pr[3];
+        memset(pr, 0, sizeof(pr));
+        for (int i = 0; i < 3; ++i) {
+            pr[i].x = dev(40 + 3 * (uintptr_t)i);
+            pr[i].packed = dev(41 + 3 * (uintptr_t)i);
+            pr[i].y = dev(42 + 3 * (uintptr_t)i);
+            pr[i].M = 1;
+            pr[i].N = 1000 + 77 * i;
+            pr[i].K = 1024 * (i + 1);
+        }
+        const size_t bytes = mnb_plan_bytes(3);
+        uint8_t *plan = (uint8_t *)malloc(bytes);
+        CHECK(mnb_plan_grouped_i8(pr, 3, 4, 32, MNB_F16, plan, bytes) == MNB_OK);
+        CHECK(mnb_plan_launches(plan) == 1);
+        pr[1].M = 2;
+        CHECK(mnb_plan_grouped_i8(pr, 3, 4, 32, MNB_F16, plan, bytes) == MNB_ERR_SHAPE);
+        free(plan);
+    }
     const size_t wsb = mnb_gemm_i8_workspace_bytes(4, 128, 32);
     CHECK(wsb >= 4 * 128 && wsb % 256 == 0);
     CHECK(mnb_gemm_i8_workspace_bytes(410, 2048, 64) >= (size_t)(410 * 2048 + 410 * 32 * 4 + 410 * 64 * 4));

@@ -103,6 +103,7 @@ def test_int8_workspace_reuse_and_smaller_call():
     _, _, _, pw = packed_case(w, 64, dt)
     xt = torch.from_numpy(x).to(DEV)
     ws = mnb.i8_workspace(40, 1024, 64, DEV)
+    assert mnb.mnb_gemm_i8_workspace_bytes(1, 1024, 64) == 0
     y1 = mnb.mnb_gemm_i8(xt, pw, ws)
     y2 = mnb.mnb_gemm_i8(xt[:9].contiguous(), pw, ws)
     torch.cuda.synchronize()
@@ -130,3 +131,96 @@ def test_int8_full_size_linears_sampled(ci, lin_index):
     ref = oracle.matmul_nbits_i8(x[rows], q[cols], zp[cols], s[cols], cfg.block_size)
     ok, err, mx = oracle.within_tolerance(y[np.ix_(rows, cols)], ref, TOL[dt])
     assert ok, f"err {err:.3e} vs {TOL[dt]} * {mx:.3e}"
+
+
+DECODE_SHAPES = [(64, 256, 32), (40, 4160, 32), (17, 96, 32), (33, 192, 64), (50, 512, 128), (70, 1024, 256),
+                 (3000, 1024, 32), (1000, 32768, 64)]
+
+
+@pytest.mark.parametrize("dt", [np.float16, np.float32])
+@pytest.mark.parametrize("n,k,bs", DECODE_SHAPES)
+def test_int8_decode_one_launch_equals_two_launch_form(n, k, bs, dt):
+    """M = 1 runs one launch that quantizes x in LDS; its outputs equal, bit
+    for bit, row 0 of a two-row call (quantize launch + product launch) on
+    [x; x], and are within tolerance of the oracle."""
+    w, x = synth.random_case(n + 3 * k, 1, n, k, "f16" if dt == np.float16 else "f32")
+    q, s, zp, pw = packed_case(w, bs, dt)
+    xt = torch.from_numpy(x).to(DEV)
+    y1 = mnb.mnb_gemm_i8(xt, pw)
+    y2 = mnb.mnb_gemm_i8(torch.cat([xt, xt]).contiguous(), pw)
+    torch.cuda.synchronize()
+    assert torch.equal(y1[0], y2[0]) and torch.equal(y2[0], y2[1])
+    ref = oracle.matmul_nbits_i8(x, q, zp, s, bs)
+    ok, err, mx = oracle.within_tolerance(y1.cpu().numpy(), ref, TOL[dt])
+    assert ok, f"err {err:.3e} vs {TOL[dt]} * {mx:.3e}"
+
+
+def test_int8_decode_planted_activations():
+    """Zero blocks, ties and extremes through the one-launch decode path."""
+    n, k, bs, dt = 48, 1024, 32, np.float16
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    x3 = planted_activations(3, k, bs, dt, seed=11)
+    q, s, zp, pw = packed_case(w, bs, dt)
+    for row in range(3):
+        x = x3[row:row + 1]
+        y = mnb.mnb_gemm_i8(torch.from_numpy(x).to(DEV), pw)
+        torch.cuda.synchronize()
+        ref = oracle.matmul_nbits_i8(x, q, zp, s, bs)
+        ok, err, mx = oracle.within_tolerance(y.cpu().numpy(), ref, TOL[dt])
+        assert ok, f"row {row}: err {err:.3e} vs {TOL[dt]} * {mx:.3e}"
+
+
+@pytest.mark.parametrize("dt", [np.float16, np.float32])
+def test_int8_grouped_plan_equals_single_calls(dt):
+    """A plan of decode products of mixed shapes (one launch): every output
+    bitwise equal to its single mnb_gemm_i8 call; products past the first of
+    a workgroup's range re-quantize their own vector."""
+    rng = np.random.default_rng(21)
+    problems, singles = [], []
+    for i in range(23):
+        n = int(rng.integers(1, 3000))
+        k = int(rng.choice([256, 1024, 2048, 4160 if dt == np.float32 else 3072]))
+        w, x = synth.random_case(700 + i, 1, n, k, "f16" if dt == np.float16 else "f32")
+        _, _, _, pw = packed_case(w, 32, dt)
+        xt = torch.from_numpy(x.reshape(-1)).to(DEV)
+        problems.append((xt, pw, None))
+        singles.append(mnb.mnb_gemm_i8(xt.reshape(1, -1), pw))
+    plan = mnb.mnb_plan_grouped(problems, 32, TD[dt], int8=True)
+    assert mnb.mnb_plan_launches(plan) == 1
+    mnb.mnb_gemm_grouped(plan)
+    torch.cuda.synchronize()
+    for i, (y, ys) in enumerate(zip(plan.outputs, singles)):
+        assert torch.equal(y.reshape(-1), ys.reshape(-1)), f"problem {i}"
+
+
+def test_int8_plan_refuses_prefill_products():
+    w, x = synth.random_case(5, 4, 32, 256, "f16")
+    _, _, _, pw = packed_case(w, 32, np.float16)
+    with pytest.raises(mnb.MnbError):
+        mnb.mnb_plan_grouped([(torch.from_numpy(x).to(DEV), pw, None)], 32, torch.float16, int8=True)
+
+
+def test_int8_full_size_decode_step_grouped():
+    """The 0.6B decode step in the int8 mode as one grouped launch (the
+    launch bench.py times): every output bitwise equal to single calls, and
+    sampled outputs of three linears (the LM head among them) within
+    tolerance of the oracle."""
+    from block_wise_int4_amd import workload
+    cfg = configs.CONFIGS[1]
+    data = workload.build_config(cfg, DEV)
+    plan = mnb.mnb_plan_grouped([(ld.x.reshape(-1), ld.pw, ld.y) for ld in data.linears], cfg.block_size,
+                                torch.float16, int8=True)
+    mnb.mnb_gemm_grouped(plan)
+    torch.cuda.synchronize()
+    for ld in data.linears:
+        single = mnb.mnb_gemm_i8(ld.x.reshape(1, -1), ld.pw)
+        assert torch.equal(single.reshape(-1), ld.y.reshape(-1)), f"{ld.lin}"
+    for ld in (data.linears[0], data.linears[6], data.linears[-1]):
+        w, x = synth.linear_inputs(cfg, ld.lin)
+        rows = np.random.default_rng(ld.lin.n).integers(0, ld.lin.n, 64)
+        q, s, zp = oracle.rtn_quantize(w[rows], cfg.block_size, np.float16)
+        ref = oracle.matmul_nbits_i8(x, q, zp, s, cfg.block_size)
+        got = ld.y.reshape(-1).cpu().numpy()[rows][None, :]
+        ok, err, mx = oracle.within_tolerance(got, ref, TOL[np.float16])
+        assert ok, f"{ld.lin}: err {err:.3e} vs {TOL[np.float16]} * {mx:.3e}"
