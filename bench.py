@@ -34,8 +34,10 @@ LLC_BYTES = 256e6              # Infinity Cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # sources each measured kernel is built from (counter data is tied to them)
 KERNEL_SOURCES = {
-    "decode_grouped_kernel": ("mnb_gemv.hip", "mnb_device.h", "mnb_layout.h", "mnb_internal.h"),
+    "decode_grouped_kernel": ("mnb_gemv.hip", "mnb_decode.h", "mnb_device.h", "mnb_layout.h", "mnb_internal.h"),
     "gemm_grouped_kernel": ("mnb_gemm.hip", "mnb_device.h", "mnb_layout.h", "mnb_internal.h"),
+    "decode_i8_grouped_kernel": ("mnb_int8.hip", "mnb_decode.h", "mnb_device.h", "mnb_layout.h",
+                                 "mnb_internal.h"),
 }
 
 
@@ -139,7 +141,7 @@ def summarize_trace(trace_csv, bench_json, command, out_dir):
     line = [ln for ln in open(bench_json).read().splitlines() if ln.startswith("{")][-1]
     res = json.loads(line)
     legs = [(res["config"]["workload"], res["roofline"], res["steps"], res["warmup"])]
-    for key in ("prefill",):
+    for key in ("prefill", "int8_mode"):
         if key in res:
             legs.append((res[key]["workload"], res[key]["roofline"], res[key]["steps"], res[key]["warmup"]))
     for name, leg in res.get("legs", {}).items():
@@ -610,13 +612,15 @@ def run_int8_mode(cfg, steps, warmup, torch, dev):
     del graphs, plans, sets, base
     torch.cuda.empty_cache()
     roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "decode_i8_grouped_kernel",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": stored_traffic(f"decode_i8_grouped_kernel:{cfg.name}"), "kernel": "decode_i8_grouped_kernel",
             "launch_us": round(ms * 1e3, 2), "algorithmic_bytes_per_launch": algo}
     if launches == 1:
         roof["launch_timing"] = "timed region / steps (one launch per step, back to back)"
     return {"workload": cfg.name, "mode": "int8 activations (per-block symmetric, quantized in LDS), "
                                           "integer dot products",
             "schedule": "grouped", "launches_per_step": launches, "replicas": replicas, "steps": steps,
+            "warmup": warmup,
             "ms_per_step": round(ms, 5), "first_launch_us": round(first_ms * 1e3, 2),
             "value": round(gbs, 2), "unit": "GB/s", "roofline": roof,
             "per_linear": {"unit": "GB/s", "graph_ms_per_step": round(pl_ms, 5),
@@ -702,12 +706,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=1, help="headline workload (index into workloads.configs)")
     ap.add_argument("--prefill-config", type=int, default=3, help="prefill workload timed alongside; -1 = none")
-    ap.add_argument("--extra-configs", default="2,4",
+    ap.add_argument("--extra-configs", default="2,4,5",
                     help="further workloads timed as legs of the line (comma-separated indices; '' = none)")
     ap.add_argument("--no-per-linear", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-next", action="store_true",
-                    help="skip the LM-head argmax, embedding-gather and int8-mode lines")
+    ap.add_argument("--no-next", action="store_true", help="skip the LM-head argmax and embedding-gather lines")
+    ap.add_argument("--no-int8", action="store_true", help="skip the int8 compute-mode line")
     ap.add_argument("--launch-events", action="store_true",
                     help="also time each launch between its own event pair (diagnostic; logged, not reported)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work per workload")
@@ -736,7 +740,8 @@ def main():
 
     if args.record_traffic:
         wl = {"decode_grouped_kernel": configs.CONFIGS[args.config].name,
-              "gemm_grouped_kernel": configs.CONFIGS[args.prefill_config].name}
+              "gemm_grouped_kernel": configs.CONFIGS[args.prefill_config].name,
+              "decode_i8_grouped_kernel": configs.CONFIGS[args.config].name}
         record_traffic(*args.record_traffic, args.copy_probe_mib or 512, wl, args.traffic_command)
         return
 
@@ -807,7 +812,7 @@ def main():
         result["lm_head_argmax"] = run_lm_head_argmax(cfg, args.steps, args.warmup, torch, dev)
         result["embedding_gather"] = run_embed_gather(cfg, args.steps, args.warmup, torch, dev)
 
-    if not args.no_next:
+    if not args.no_int8 and cfg.m == 1:
         result["int8_mode"] = run_int8_mode(cfg, args.steps, args.warmup, torch, dev)
 
     if args.prefill_config >= 0:
