@@ -166,7 +166,8 @@ int mnb_gemm_i8(const void *x, const void *packed, void *y, void *workspace, siz
     if (!aligned16(workspace)) return MNB_ERR_ALIGN;
     if (workspace_bytes < (size_t)a8_workspace_bytes(M, K, block_size)) return MNB_ERR_INVALID;
     const Problem p = make_problem(x, packed, y, M, N, K, block_size, dtype_bytes(dtype));
-    if ((M * (K / 8) + 255) / 256 > 0x7FFFFFFFLL || gemm_i8_workgroups(p) > 0x7FFFFFFFLL) return MNB_ERR_SHAPE;
+    if ((M * (K / 8) + 255) / 256 > 0x7FFFFFFFLL || gemm_i8_workgroups(p) > 0x7FFFFFFFLL || !gemm_i8_fits(p))
+        return MNB_ERR_SHAPE;
     return hip_status(launch_gemm_i8(p, dtype, workspace, as_stream(stream)));
 }
 

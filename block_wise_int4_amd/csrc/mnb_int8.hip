@@ -71,10 +71,11 @@ __device__ __forceinline__ uint2 quantize8(const float (&v)[8], int bs, float *a
     return uint2{word[0], word[1]};
 }
 
+// scales: [m][K / bs], or with m_pad > 0 transposed, [K / bs][m_pad]
 template <typename T, bool kDeviceOrder>
 __global__ __launch_bounds__(256) void quantize_act_kernel(const T *__restrict__ x, int64_t m_rows, int64_t k, int bs,
                                                            int8_t *__restrict__ qa, float *__restrict__ scales,
-                                                           int32_t *__restrict__ chunk_sums) {
+                                                           int32_t *__restrict__ chunk_sums, int64_t m_pad) {
     // thread = 8 consecutive inputs; the bs / 8 threads of a block are
     // consecutive lanes of one wave (bs divides 256, 8 divides bs)
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -90,7 +91,10 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const T *__restrict__
     const uint2 word = quantize8<kDeviceOrder>(v, bs, &a_s, &sum);
     if (!live) return;
     *reinterpret_cast<uint2 *>(qa + m * k + k0) = word;
-    if (k0 % bs == 0) scales[m * (k / bs) + k0 / bs] = a_s;
+    if (k0 % bs == 0) {
+        if (m_pad > 0) scales[(k0 / bs) * m_pad + m] = a_s;
+        else scales[m * (k / bs) + k0 / bs] = a_s;
+    }
     if (chunk_sums && k0 % kChunk == 0) chunk_sums[m * (k / kChunk) + k0 / kChunk] = sum;
 }
 
@@ -98,11 +102,16 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const T *__restrict__
 struct A8Workspace {
     int64_t qa_bytes, scales_off, sums_off, total;
 };
+// The matrix-core path (M >= kA8MfmaMinRows) reads the activation scales
+// transposed, [K / bs][m_pad], m_pad = M rounded up to whole row tiles.
+constexpr int kA8MfmaMinRows = 16;
+constexpr int kA8MPad = 128;
+inline int64_t a8_m_pad(int64_t m) { return align_up(m, kA8MPad); }
 inline A8Workspace a8_workspace(int64_t m, int64_t k, int bs) {
     A8Workspace w;
     w.qa_bytes = m * k;
     w.scales_off = align_up(w.qa_bytes, kAlign);
-    w.sums_off = align_up(w.scales_off + m * (k / bs) * 4, kAlign);
+    w.sums_off = align_up(w.scales_off + a8_m_pad(m) * (k / bs) * 4, kAlign);
     w.total = align_up(w.sums_off + m * (k / kChunk) * 4, kAlign);
     return w;
 }
@@ -171,6 +180,149 @@ __global__ __launch_bounds__(64 * kA8Waves) void i8_rows_kernel(Problem p, const
             if (m0 + i < p.m) y[(m0 + i) * p.n + n] = Io<T>::from_f32(acc[i]);
     }
 }
+
+// ---------------------------------------------------------------------------
+// M >= 16: the int8 matrix-core kernel.
+//
+// v_mfma_i32_16x16x32_i8 takes, per lane, 8 bytes of A (activation row
+// lane & 15) and 8 bytes of B (weight row lane & 15) for the same 8 of its
+// 32 K positions (lane group lane >> 4). A lane loads word g = lane >> 4 of
+// its weight row's 32-input chunk (8 codes, k0 k2 k4 k6 k1 k3 k5 k7) and
+// expands it to bytes with two masks (k0 k4 k1 k5 | k2 k6 k3 k7); the
+// quantizer stores the activations in that same byte order, so one MFMA is
+// exactly one 32-input chunk of both operands, and chunks of one block never
+// mix with another block's. The zero point is folded into the bytes:
+// (nibble + 0x80 - zp) ^ 0x80 is nibble - zp as a signed byte, four at a
+// time with no carries. A block's chunks chain into one integer accumulator
+// (exact: |sum| <= 256 * 15 * 127); at the block's end each of the lane's 4
+// outputs takes s[n] * a_s[m] * sum in float32.
+// Workgroup: 2 x 2 waves, a wave computes (MF * 16) x (NF * 16) outputs.
+// ---------------------------------------------------------------------------
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int64_t a8_xcd_logical_wg(int64_t b, int64_t n) {
+    // block b runs on XCD b % 8; give each XCD a contiguous range of tiles
+    const int64_t q = n / 8, rem = n % 8;
+    const int64_t x = b % 8, i = b / 8;
+    return x * q + (x < rem ? x : rem) + i;
+}
+
+template <typename T, int MF, int NF>
+__global__ __launch_bounds__(256) void i8_mfma_kernel(Problem p, const int8_t *__restrict__ qa,
+                                                      const float *__restrict__ a_scales_t, int64_t m_pad) {
+    constexpr int WM = 2, WN = 2;
+    const int64_t tiles_n = (p.rg + WN * NF - 1) / (WN * NF);
+    const int64_t wg = a8_xcd_logical_wg(blockIdx.x, gridDim.x);
+    const int64_t tn = wg % tiles_n, tm = wg / tiles_n;
+    const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, grp = lane >> 4;
+    const int wm = wave / WN, wn = wave % WN;
+    const int64_t m_base = (tm * WM + wm) * MF * 16;   // the wave's first activation row
+    const int64_t g_base = (tn * WN + wn) * NF;        // the wave's first weight row group
+    const int sh = __builtin_ctz((unsigned)p.bs);
+    const int64_t nb = p.k >> sh;
+    // rows past M read zero (buffer range); row groups past N have an empty range
+    const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t *>(qa), 0, (int)(p.m * p.k), 0x00020000);
+    const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(a_scales_t), 0, (int)(nb * m_pad * 4), 0x00020000);
+    __amdgpu_buffer_rsrc_t cr[NF];
+#pragma unroll
+    for (int b = 0; b < NF; ++b) {
+        const int64_t g = g_base + b;
+        const bool in = g < p.rg;
+        cr[b] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(p.packed + (in ? g : 0) * p.kg * kTileCodeBytes),
+                                                  0, in ? (int)(p.kg * kTileCodeBytes) : 0, 0x00020000);
+    }
+    const T *wscale = reinterpret_cast<const T *>(p.packed + p.scales_off);
+    float acc[MF][NF][4];
+    i32x4 ci[MF][NF];
+#pragma unroll
+    for (int a = 0; a < MF; ++a)
+#pragma unroll
+        for (int b = 0; b < NF; ++b) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[a][b][i] = 0.0f;
+            ci[a][b] = i32x4{0, 0, 0, 0};
+        }
+    float s[NF];
+    uint32_t zb[NF];
+    for (int64_t c = 0; c < p.kg; ++c) {
+        for (int k32 = 0; k32 < kTileK / kChunk; ++k32) {
+            const int64_t kk = c * kTileK + k32 * kChunk;  // the chunk's first input (uniform)
+            if (kk >= p.k) break;
+            if ((kk & (p.bs - 1)) == 0) {  // a block starts: its weight scales and zero points
+                const int e = (p.bs >= kTileK ? 0 : (k32 * kChunk) >> sh) * kTileRows + r;
+#pragma unroll
+                for (int b = 0; b < NF; ++b) {
+                    const int64_t g = g_base + b;
+                    float sv = 0.0f;
+                    uint32_t zp = 0;
+                    if (g < p.rg) {
+                        const int64_t mi = meta_index(g, p.nbt, p.kgp, e, c);
+                        sv = Io<T>::to_f32(wscale[mi]);
+                        zp = (p.packed[p.zp_off + (mi >> 1)] >> (4 * (mi & 1))) & 15u;
+                    }
+                    s[b] = sv;
+                    zb[b] = (0x80u - zp) * 0x01010101u;
+                }
+            }
+            long bop[NF];
+#pragma unroll
+            for (int b = 0; b < NF; ++b) {
+                const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(
+                    cr[b], (int)(c * kTileCodeBytes) + (k32 * kTileRows + r) * 16 + grp * 4, 0, 0);
+                const uint32_t lo = ((w & 0x0F0F0F0Fu) + zb[b]) ^ 0x80808080u;
+                const uint32_t hi = (((w >> 4) & 0x0F0F0F0Fu) + zb[b]) ^ 0x80808080u;
+                bop[b] = (long)(((uint64_t)hi << 32) | lo);
+            }
+#pragma unroll
+            for (int a = 0; a < MF; ++a) {
+                const int64_t m = m_base + a * 16 + r;
+                const uint32_t off = (uint32_t)(m * p.k + kk + grp * 8);
+                const u32x2 av = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(ar, (int)off, 0, 0));
+                const long aop = (long)(((uint64_t)av.y << 32) | av.x);
+#pragma unroll
+                for (int b = 0; b < NF; ++b) ci[a][b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop[b], ci[a][b], 0, 0, 0);
+            }
+            if (((kk + kChunk) & (p.bs - 1)) == 0) {  // the block ends: scale its integer sums
+                const int64_t blk = kk >> sh;
+#pragma unroll
+                for (int a = 0; a < MF; ++a) {
+                    const uint32_t soff = (uint32_t)((blk * m_pad + m_base + a * 16 + grp * 4) * 4);
+                    // (the whole vector is reinterpreted: a bit cast of one element of a
+                    // vector, v.y, reads element 0 with this compiler)
+                    const f4 as4 = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(sr, (int)soff, 0, 0));
+                    const float asv[4] = {as4.x, as4.y, as4.z, as4.w};
+#pragma unroll
+                    for (int b = 0; b < NF; ++b) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[a][b][i] = __builtin_fmaf(s[b] * asv[i], (float)ci[a][b][i], acc[a][b][i]);
+                        ci[a][b] = i32x4{0, 0, 0, 0};
+                    }
+                }
+            }
+        }
+    }
+    T *y = static_cast<T *>(p.y);
+#pragma unroll
+    for (int b = 0; b < NF; ++b) {
+        const int64_t n = (g_base + b) * kTileRows + r;
+        if (n >= p.n) continue;
+#pragma unroll
+        for (int a = 0; a < MF; ++a)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t m = m_base + a * 16 + grp * 4 + i;
+                if (m < p.m) y[m * p.n + n] = Io<T>::from_f32(acc[a][b][i]);
+            }
+    }
+}
+
+constexpr int kA8MF = 2, kA8NF = 2;  // wave tile 32 x 32, workgroup tile 64 x 64
 
 // ---------------------------------------------------------------------------
 // M = 1: the decode-shaped int8 kernel.
@@ -376,10 +528,10 @@ hipError_t launch_quantize_act(const void *x, int64_t m, int64_t k, int bs, int 
     const unsigned grid = grid_256(m * (k / 8));
     if (dtype == kF16)
         quantize_act_kernel<_Float16, false><<<grid, 256, 0, st>>>(static_cast<const _Float16 *>(x), m, k, bs, qa,
-                                                                   scales, nullptr);
+                                                                   scales, nullptr, 0);
     else
         quantize_act_kernel<float, false><<<grid, 256, 0, st>>>(static_cast<const float *>(x), m, k, bs, qa, scales,
-                                                                nullptr);
+                                                                nullptr, 0);
     return hipGetLastError();
 }
 
@@ -390,14 +542,22 @@ hipError_t launch_gemm_i8(const Problem &p, int dtype, void *workspace, hipStrea
     float *a_s = reinterpret_cast<float *>(base + ws.scales_off);
     int32_t *sums = reinterpret_cast<int32_t *>(base + ws.sums_off);
     const unsigned qgrid = grid_256(p.m * (p.k / 8));
+    const bool mfma = p.m >= kA8MfmaMinRows;
+    const int64_t m_pad = mfma ? a8_m_pad(p.m) : 0;  // the matrix-core kernel reads the scales transposed
     if (dtype == kF16)
         quantize_act_kernel<_Float16, true><<<qgrid, 256, 0, st>>>(static_cast<const _Float16 *>(p.x), p.m, p.k,
-                                                                   p.bs, qa, a_s, sums);
+                                                                   p.bs, qa, a_s, sums, m_pad);
     else
         quantize_act_kernel<float, true><<<qgrid, 256, 0, st>>>(static_cast<const float *>(p.x), p.m, p.k, p.bs, qa,
-                                                                a_s, sums);
+                                                                a_s, sums, m_pad);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (mfma) {
+        const unsigned grid = (unsigned)gemm_i8_workgroups(p);
+        if (dtype == kF16) i8_mfma_kernel<_Float16, kA8MF, kA8NF><<<grid, 256, 0, st>>>(p, qa, a_s, m_pad);
+        else i8_mfma_kernel<float, kA8MF, kA8NF><<<grid, 256, 0, st>>>(p, qa, a_s, m_pad);
+        return hipGetLastError();
+    }
     const int64_t groups = (p.rg + kA8Waves - 1) / kA8Waves;
     if (p.m >= 4) {
         const unsigned grid = (unsigned)(groups * ((p.m + 3) / 4));
@@ -411,7 +571,19 @@ hipError_t launch_gemm_i8(const Problem &p, int dtype, void *workspace, hipStrea
     return hipGetLastError();
 }
 
+// The matrix-core path addresses the activations and their scales with
+// 32-bit buffer offsets.
+bool gemm_i8_fits(const Problem &p) {
+    if (p.m < kA8MfmaMinRows) return true;
+    return p.m * p.k < 0x7FFFFFFFLL && (p.k / p.bs) * a8_m_pad(p.m) * 4 < 0x7FFFFFFFLL;
+}
+
 int64_t gemm_i8_workgroups(const Problem &p) {
+    if (p.m >= kA8MfmaMinRows) {
+        const int64_t tiles_n = (p.rg + 2 * kA8NF - 1) / (2 * kA8NF);
+        const int64_t tiles_m = (p.m + 2 * kA8MF * 16 - 1) / (2 * kA8MF * 16);
+        return tiles_m * tiles_n;
+    }
     const int64_t groups = (p.rg + kA8Waves - 1) / kA8Waves;
     return p.m >= 4 ? groups * ((p.m + 3) / 4) : groups * p.m;
 }

@@ -133,6 +133,7 @@ hipError_t launch_gemv_grouped(const Problem *dev_entries, int count, const Gemv
 // workspace holds them), integer dot products with the 4-bit codes.
 int64_t a8_workspace_bytes(int64_t m, int64_t k, int bs);
 int64_t gemm_i8_workgroups(const Problem &p);
+bool gemm_i8_fits(const Problem &p);  // the problem's offsets fit the kernels' 32-bit addressing
 hipError_t launch_quantize_act(const void *x, int64_t m, int64_t k, int bs, int dtype, int8_t *qa, float *scales,
                                hipStream_t st);
 hipError_t launch_gemm_i8(const Problem &p, int dtype, void *workspace, hipStream_t st);

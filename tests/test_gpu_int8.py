@@ -66,7 +66,10 @@ def test_activation_quantizer_bit_exact(m, k, bs, dt):
 
 
 PSHAPES = [(1, 64, 256, 32), (1, 40, 4160, 32), (2, 17, 96, 32), (3, 33, 192, 64), (4, 64, 512, 128),
-           (7, 50, 512, 256), (16, 130, 640, 64), (62, 96, 1024, 32), (410, 48, 2048, 64)]
+           (7, 50, 512, 256), (15, 40, 256, 32),
+           # M >= 16: the matrix-core kernel (ragged M and N, K tails, blocks spanning two tiles)
+           (16, 130, 640, 64), (17, 16, 128, 128), (40, 70, 4160, 32), (62, 96, 1024, 32), (64, 33, 512, 256),
+           (100, 200, 1536, 128), (410, 48, 2048, 64)]
 
 
 @pytest.mark.parametrize("dt", [np.float16, np.float32])
@@ -96,8 +99,10 @@ def test_int8_product_symmetric_weights(dt):
 
 
 def test_int8_workspace_reuse_and_smaller_call():
-    """One workspace serves a call and then a smaller one; both match the
-    calls made with workspaces of their own."""
+    """One workspace serves a call and then smaller ones (the matrix-core
+    kernel at M = 40 and 20, the vector kernel at M = 9); each matches the
+    call made with a workspace of its own, and a row's bits do not depend on
+    how many rows the call has (within one kernel)."""
     dt = np.float16
     w, x = synth.random_case(42, 40, 80, 1024, "f16")
     _, _, _, pw = packed_case(w, 64, dt)
@@ -105,11 +110,18 @@ def test_int8_workspace_reuse_and_smaller_call():
     ws = mnb.i8_workspace(40, 1024, 64, DEV)
     assert mnb.mnb_gemm_i8_workspace_bytes(1, 1024, 64) == 0
     y1 = mnb.mnb_gemm_i8(xt, pw, ws)
-    y2 = mnb.mnb_gemm_i8(xt[:9].contiguous(), pw, ws)
+    y2 = mnb.mnb_gemm_i8(xt[:20].contiguous(), pw, ws)
+    y3 = mnb.mnb_gemm_i8(xt[:9].contiguous(), pw, ws)
     torch.cuda.synchronize()
     assert torch.equal(y1, mnb.mnb_gemm_i8(xt, pw))
-    assert torch.equal(y2, mnb.mnb_gemm_i8(xt[:9].contiguous(), pw))
-    assert torch.equal(y2, y1[:9])
+    assert torch.equal(y2, mnb.mnb_gemm_i8(xt[:20].contiguous(), pw))
+    assert torch.equal(y3, mnb.mnb_gemm_i8(xt[:9].contiguous(), pw))
+    assert torch.equal(y2, y1[:20])
+    y4 = mnb.mnb_gemm_i8(xt[:5].contiguous(), pw, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y4, y3[:5])
+    ok, err, mx = oracle.within_tolerance(y3.float().cpu().numpy(), y1[:9].float().cpu().numpy(), TOL[dt])
+    assert ok, f"vector and matrix-core kernels differ by {err:.3e} (max {mx:.3e})"
 
 
 @pytest.mark.parametrize("ci,lin_index", [(0, 0), (1, 3), (3, 6), (4, 1)])
