@@ -71,11 +71,16 @@ __device__ __forceinline__ uint2 quantize8(const float (&v)[8], int bs, float *a
     return uint2{word[0], word[1]};
 }
 
-// scales: [m][K / bs], or with m_pad > 0 transposed, [K / bs][m_pad]
+// scales: [m][K / bs], or with m_pad > 0 transposed, [K / bs][m_pad].
+// With m_pad > 0 the codes also take the matrix-core kernel's order: rows
+// of qa_stride bytes (K rounded up to whole tiles), and inside each
+// 128-input tile the 8-byte pieces of chunk k32, lane group g at position
+// g * 4 + k32 (a lane's four pieces of a tile are contiguous).
 template <typename T, bool kDeviceOrder>
 __global__ __launch_bounds__(256) void quantize_act_kernel(const T *__restrict__ x, int64_t m_rows, int64_t k, int bs,
                                                            int8_t *__restrict__ qa, float *__restrict__ scales,
-                                                           int32_t *__restrict__ chunk_sums, int64_t m_pad) {
+                                                           int32_t *__restrict__ chunk_sums, int64_t m_pad,
+                                                           int64_t qa_stride) {
     // thread = 8 consecutive inputs; the bs / 8 threads of a block are
     // consecutive lanes of one wave (bs divides 256, 8 divides bs)
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -90,7 +95,13 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(const T *__restrict__
     int sum;
     const uint2 word = quantize8<kDeviceOrder>(v, bs, &a_s, &sum);
     if (!live) return;
-    *reinterpret_cast<uint2 *>(qa + m * k + k0) = word;
+    if (m_pad > 0) {
+        const int64_t t8 = (k0 % kTileK) / 8;  // = k32 * 4 + g
+        const int64_t pos = (k0 / kTileK) * kTileK + ((t8 % 4) * 4 + t8 / 4) * 8;
+        *reinterpret_cast<uint2 *>(qa + m * qa_stride + pos) = word;
+    } else {
+        *reinterpret_cast<uint2 *>(qa + m * k + k0) = word;
+    }
     if (k0 % bs == 0) {
         if (m_pad > 0) scales[(k0 / bs) * m_pad + m] = a_s;
         else scales[m * (k / bs) + k0 / bs] = a_s;
@@ -109,7 +120,7 @@ constexpr int kA8MPad = 128;
 inline int64_t a8_m_pad(int64_t m) { return align_up(m, kA8MPad); }
 inline A8Workspace a8_workspace(int64_t m, int64_t k, int bs) {
     A8Workspace w;
-    w.qa_bytes = m * k;
+    w.qa_bytes = m * align_up(k, kTileK);  // rows padded to whole tiles for the matrix-core kernel
     w.scales_off = align_up(w.qa_bytes, kAlign);
     w.sums_off = align_up(w.scales_off + a8_m_pad(m) * (k / bs) * 4, kAlign);
     w.total = align_up(w.sums_off + m * (k / kChunk) * 4, kAlign);
@@ -208,10 +219,27 @@ __device__ __forceinline__ int64_t a8_xcd_logical_wg(int64_t b, int64_t n) {
     return x * q + (x < rem ? x : rem) + i;
 }
 
-template <typename T, int MF, int NF>
-__global__ __launch_bounds__(256) void i8_mfma_kernel(Problem p, const int8_t *__restrict__ qa,
+// Inputs of one 128-input tile for a wave: per weight row group its 4 code
+// words (one per 32-input chunk), per activation fragment its 32 bytes (the
+// quantizer groups a lane's four 8-byte pieces of a tile together), and the
+// scales and zero points of the tile's blocks.
+template <int BS, int MF, int NF>
+struct A8Tile {
+    static constexpr int kBlocks = BS >= kTileK ? 1 : kTileK / BS;  // blocks (or parts of one) per tile
+    uint32_t w[NF][4];
+    u32x4 a[MF][2];
+    f4 as[MF][kBlocks];
+    float s[NF][kBlocks];
+    uint32_t zb[NF][kBlocks];  // (0x80 - zp) in every byte
+};
+
+template <typename T, int BS, int MF, int NF>
+__global__ __launch_bounds__(256) void i8_mfma_kernel(Problem p, const int8_t *__restrict__ qa, int64_t qa_stride,
                                                       const float *__restrict__ a_scales_t, int64_t m_pad) {
     constexpr int WM = 2, WN = 2;
+    using Tile = A8Tile<BS, MF, NF>;
+    constexpr int kBlocks = Tile::kBlocks;
+    constexpr int kChunksPerBlock = BS / kChunk;
     const int64_t tiles_n = (p.rg + WN * NF - 1) / (WN * NF);
     const int64_t wg = a8_xcd_logical_wg(blockIdx.x, gridDim.x);
     const int64_t tn = wg % tiles_n, tm = wg / tiles_n;
@@ -221,11 +249,10 @@ __global__ __launch_bounds__(256) void i8_mfma_kernel(Problem p, const int8_t *_
     const int wm = wave / WN, wn = wave % WN;
     const int64_t m_base = (tm * WM + wm) * MF * 16;   // the wave's first activation row
     const int64_t g_base = (tn * WN + wn) * NF;        // the wave's first weight row group
-    const int sh = __builtin_ctz((unsigned)p.bs);
-    const int64_t nb = p.k >> sh;
+    const int64_t nb = p.k / BS;
     // rows past M read zero (buffer range); row groups past N have an empty range
     const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t *>(qa), 0, (int)(p.m * p.k), 0x00020000);
+        const_cast<int8_t *>(qa), 0, (int)(p.m * qa_stride), 0x00020000);
     const __amdgpu_buffer_rsrc_t sr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(a_scales_t), 0, (int)(nb * m_pad * 4), 0x00020000);
     __amdgpu_buffer_rsrc_t cr[NF];
@@ -236,7 +263,64 @@ __global__ __launch_bounds__(256) void i8_mfma_kernel(Problem p, const int8_t *_
         cr[b] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(p.packed + (in ? g : 0) * p.kg * kTileCodeBytes),
                                                   0, in ? (int)(p.kg * kTileCodeBytes) : 0, 0x00020000);
     }
-    const T *wscale = reinterpret_cast<const T *>(p.packed + p.scales_off);
+    // each row group's scales and zero points: one contiguous metadata span
+    // (empty for row groups past N, whose loads then read zero)
+    const int64_t meta_span = (p.kgp / kMetaGroup) * (int64_t)p.nbt * kTileRows * kMetaGroup;  // entries
+    __amdgpu_buffer_rsrc_t msr[NF], mzr[NF];
+#pragma unroll
+    for (int b = 0; b < NF; ++b) {
+        const int64_t g = g_base + b;
+        const bool in = g < p.rg;
+        const int64_t first = (in ? g : 0) * meta_span;
+        msr[b] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(p.packed + p.scales_off + first * sizeof(T)), 0,
+                                                   in ? (int)(meta_span * sizeof(T)) : 0, 0x00020000);
+        mzr[b] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(p.packed + p.zp_off + first / 2), 0,
+                                                   in ? (int)(meta_span / 2) : 0, 0x00020000);
+    }
+
+    // every load is issued for every tile (a tile past K reads zeros or
+    // unused bytes inside the buffers), so the compiler counts them exactly
+    auto load_tile = [&](int64_t c, Tile &t) {
+        const int64_t cm = c < p.kg ? c : p.kg - 1;  // metadata index kept inside the layout
+#pragma unroll
+        for (int b = 0; b < NF; ++b)
+#pragma unroll
+            for (int k32 = 0; k32 < 4; ++k32)
+                t.w[b][k32] = __builtin_amdgcn_raw_buffer_load_b32(
+                    cr[b], (int)(c * kTileCodeBytes) + (k32 * kTileRows + r) * 16 + grp * 4, 0, 0);
+#pragma unroll
+        for (int a = 0; a < MF; ++a) {
+            const uint32_t off = (uint32_t)((m_base + a * 16 + r) * qa_stride + c * kTileK + grp * 32);
+            t.a[a][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ar, (int)off, 0, 0));
+            t.a[a][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ar, (int)off + 16, 0, 0));
+        }
+#pragma unroll
+        for (int jb = 0; jb < kBlocks; ++jb) {
+            const int64_t blk = BS >= kTileK ? c * kTileK / BS : c * kBlocks + jb;
+#pragma unroll
+            for (int a = 0; a < MF; ++a) {
+                const uint32_t soff = (uint32_t)((blk * m_pad + m_base + a * 16 + grp * 4) * 4);
+                t.as[a][jb] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(sr, (int)soff, 0, 0));
+            }
+            // entry of (this lane's row, block jb) of tile cm inside a row group's span
+            const int64_t li = ((cm / kMetaGroup) * p.nbt * kTileRows + jb * kTileRows + r) * kMetaGroup +
+                               cm % kMetaGroup;
+#pragma unroll
+            for (int b = 0; b < NF; ++b) {
+                float sv;
+                if constexpr (sizeof(T) == 2)
+                    sv = (float)__builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                                                 msr[b], (int)(li * 2), 0, 0));
+                else
+                    sv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(msr[b], (int)(li * 4), 0, 0));
+                const uint32_t zbyte = __builtin_amdgcn_raw_buffer_load_b8(mzr[b], (int)(li >> 1), 0, 0);
+                const uint32_t zp = (zbyte >> (4 * (uint32_t)(li & 1))) & 15u;
+                t.s[b][jb] = sv;
+                t.zb[b][jb] = 0x80808080u - zp * 0x01010101u;
+            }
+        }
+    };
+
     float acc[MF][NF][4];
     i32x4 ci[MF][NF];
 #pragma unroll
@@ -247,66 +331,55 @@ __global__ __launch_bounds__(256) void i8_mfma_kernel(Problem p, const int8_t *_
             for (int i = 0; i < 4; ++i) acc[a][b][i] = 0.0f;
             ci[a][b] = i32x4{0, 0, 0, 0};
         }
-    float s[NF];
-    uint32_t zb[NF];
-    for (int64_t c = 0; c < p.kg; ++c) {
-        for (int k32 = 0; k32 < kTileK / kChunk; ++k32) {
-            const int64_t kk = c * kTileK + k32 * kChunk;  // the chunk's first input (uniform)
-            if (kk >= p.k) break;
-            if ((kk & (p.bs - 1)) == 0) {  // a block starts: its weight scales and zero points
-                const int e = (p.bs >= kTileK ? 0 : (k32 * kChunk) >> sh) * kTileRows + r;
+    auto compute_tile = [&](int64_t c, const Tile &t) {
 #pragma unroll
-                for (int b = 0; b < NF; ++b) {
-                    const int64_t g = g_base + b;
-                    float sv = 0.0f;
-                    uint32_t zp = 0;
-                    if (g < p.rg) {
-                        const int64_t mi = meta_index(g, p.nbt, p.kgp, e, c);
-                        sv = Io<T>::to_f32(wscale[mi]);
-                        zp = (p.packed[p.zp_off + (mi >> 1)] >> (4 * (mi & 1))) & 15u;
-                    }
-                    s[b] = sv;
-                    zb[b] = (0x80u - zp) * 0x01010101u;
-                }
-            }
+        for (int k32 = 0; k32 < 4; ++k32) {
+            const int64_t kk = c * kTileK + k32 * kChunk;  // the chunk's first input (uniform)
+            if (kk >= p.k) break;                          // the K tail lies on whole chunks
+            const int jb = BS >= kTileK ? 0 : k32 / kChunksPerBlock;
             long bop[NF];
 #pragma unroll
             for (int b = 0; b < NF; ++b) {
-                const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(
-                    cr[b], (int)(c * kTileCodeBytes) + (k32 * kTileRows + r) * 16 + grp * 4, 0, 0);
-                const uint32_t lo = ((w & 0x0F0F0F0Fu) + zb[b]) ^ 0x80808080u;
-                const uint32_t hi = (((w >> 4) & 0x0F0F0F0Fu) + zb[b]) ^ 0x80808080u;
+                const uint32_t w = t.w[b][k32];
+                const uint32_t lo = ((w & 0x0F0F0F0Fu) + t.zb[b][jb]) ^ 0x80808080u;
+                const uint32_t hi = (((w >> 4) & 0x0F0F0F0Fu) + t.zb[b][jb]) ^ 0x80808080u;
                 bop[b] = (long)(((uint64_t)hi << 32) | lo);
             }
 #pragma unroll
             for (int a = 0; a < MF; ++a) {
-                const int64_t m = m_base + a * 16 + r;
-                const uint32_t off = (uint32_t)(m * p.k + kk + grp * 8);
-                const u32x2 av = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(ar, (int)off, 0, 0));
-                const long aop = (long)(((uint64_t)av.y << 32) | av.x);
+                const u32x4 v = t.a[a][k32 >> 1];
+                const uint32_t x0 = (k32 & 1) ? v.z : v.x, x1 = (k32 & 1) ? v.w : v.y;
+                const long aop = (long)(((uint64_t)x1 << 32) | x0);
 #pragma unroll
-                for (int b = 0; b < NF; ++b) ci[a][b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop[b], ci[a][b], 0, 0, 0);
+                for (int b = 0; b < NF; ++b)
+                    ci[a][b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop[b], ci[a][b], 0, 0, 0);
             }
-            if (((kk + kChunk) & (p.bs - 1)) == 0) {  // the block ends: scale its integer sums
-                const int64_t blk = kk >> sh;
+            if (((kk + kChunk) % BS) == 0) {  // the block ends: scale its integer sums
 #pragma unroll
                 for (int a = 0; a < MF; ++a) {
-                    const uint32_t soff = (uint32_t)((blk * m_pad + m_base + a * 16 + grp * 4) * 4);
-                    // (the whole vector is reinterpreted: a bit cast of one element of a
-                    // vector, v.y, reads element 0 with this compiler)
-                    const f4 as4 = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(sr, (int)soff, 0, 0));
+                    const f4 as4 = t.as[a][jb];
                     const float asv[4] = {as4.x, as4.y, as4.z, as4.w};
 #pragma unroll
                     for (int b = 0; b < NF; ++b) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            acc[a][b][i] = __builtin_fmaf(s[b] * asv[i], (float)ci[a][b][i], acc[a][b][i]);
+                            acc[a][b][i] = __builtin_fmaf(t.s[b][jb] * asv[i], (float)ci[a][b][i], acc[a][b][i]);
                         ci[a][b] = i32x4{0, 0, 0, 0};
                     }
                 }
             }
         }
+    };
+
+    Tile t0, t1;
+    load_tile(0, t0);
+    for (int64_t c = 0; c < p.kg; c += 2) {
+        load_tile(c + 1, t1);
+        compute_tile(c, t0);
+        load_tile(c + 2, t0);
+        if (c + 1 < p.kg) compute_tile(c + 1, t1);
     }
+
     T *y = static_cast<T *>(p.y);
 #pragma unroll
     for (int b = 0; b < NF; ++b) {
@@ -528,10 +601,10 @@ hipError_t launch_quantize_act(const void *x, int64_t m, int64_t k, int bs, int 
     const unsigned grid = grid_256(m * (k / 8));
     if (dtype == kF16)
         quantize_act_kernel<_Float16, false><<<grid, 256, 0, st>>>(static_cast<const _Float16 *>(x), m, k, bs, qa,
-                                                                   scales, nullptr, 0);
+                                                                   scales, nullptr, 0, k);
     else
         quantize_act_kernel<float, false><<<grid, 256, 0, st>>>(static_cast<const float *>(x), m, k, bs, qa, scales,
-                                                                nullptr, 0);
+                                                                nullptr, 0, k);
     return hipGetLastError();
 }
 
@@ -544,18 +617,32 @@ hipError_t launch_gemm_i8(const Problem &p, int dtype, void *workspace, hipStrea
     const unsigned qgrid = grid_256(p.m * (p.k / 8));
     const bool mfma = p.m >= kA8MfmaMinRows;
     const int64_t m_pad = mfma ? a8_m_pad(p.m) : 0;  // the matrix-core kernel reads the scales transposed
+    const int64_t qa_stride = mfma ? p.kg * kTileK : p.k;
     if (dtype == kF16)
         quantize_act_kernel<_Float16, true><<<qgrid, 256, 0, st>>>(static_cast<const _Float16 *>(p.x), p.m, p.k,
-                                                                   p.bs, qa, a_s, sums, m_pad);
+                                                                   p.bs, qa, a_s, sums, m_pad, qa_stride);
     else
         quantize_act_kernel<float, true><<<qgrid, 256, 0, st>>>(static_cast<const float *>(p.x), p.m, p.k, p.bs, qa,
-                                                                a_s, sums, m_pad);
+                                                                a_s, sums, m_pad, qa_stride);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (mfma) {
         const unsigned grid = (unsigned)gemm_i8_workgroups(p);
-        if (dtype == kF16) i8_mfma_kernel<_Float16, kA8MF, kA8NF><<<grid, 256, 0, st>>>(p, qa, a_s, m_pad);
-        else i8_mfma_kernel<float, kA8MF, kA8NF><<<grid, 256, 0, st>>>(p, qa, a_s, m_pad);
+#define MNB_I8_MFMA(BS)                                                                                       \
+    case BS:                                                                                                  \
+        if (dtype == kF16)                                                                                    \
+            i8_mfma_kernel<_Float16, BS, kA8MF, kA8NF><<<grid, 256, 0, st>>>(p, qa, qa_stride, a_s, m_pad);   \
+        else                                                                                                  \
+            i8_mfma_kernel<float, BS, kA8MF, kA8NF><<<grid, 256, 0, st>>>(p, qa, qa_stride, a_s, m_pad);      \
+        break;
+        switch (p.bs) {
+            MNB_I8_MFMA(32)
+            MNB_I8_MFMA(64)
+            MNB_I8_MFMA(128)
+            MNB_I8_MFMA(256)
+        default: return hipErrorInvalidValue;
+        }
+#undef MNB_I8_MFMA
         return hipGetLastError();
     }
     const int64_t groups = (p.rg + kA8Waves - 1) / kA8Waves;
@@ -575,7 +662,7 @@ hipError_t launch_gemm_i8(const Problem &p, int dtype, void *workspace, hipStrea
 // 32-bit buffer offsets.
 bool gemm_i8_fits(const Problem &p) {
     if (p.m < kA8MfmaMinRows) return true;
-    return p.m * p.k < 0x7FFFFFFFLL && (p.k / p.bs) * a8_m_pad(p.m) * 4 < 0x7FFFFFFFLL;
+    return p.m * p.kg * kTileK < 0x7FFFFFFFLL && (p.k / p.bs) * a8_m_pad(p.m) * 4 < 0x7FFFFFFFLL;
 }
 
 int64_t gemm_i8_workgroups(const Problem &p) {
