@@ -627,6 +627,35 @@ def run_int8_mode(cfg, steps, warmup, torch, dev):
                            "graph": round(algo / (pl_ms * 1e-3) / 1e9, 2)}}
 
 
+def run_int8_prefill(cfg, steps, warmup, torch, dev):
+    """A prefill workload in the int8 compute mode: one mnb_gemm_i8 call per
+    linear (the activation quantizer, then the int8 matrix-core product),
+    issued back to back with one shared workspace. Rate: algorithmic
+    operations (2 M N K) per second."""
+    from block_wise_int4_amd import mnb, workload
+
+    base = workload.build_config(cfg, dev).linears
+    flops = workload.flops(cfg)
+    need = max(mnb.mnb_gemm_i8_workspace_bytes(cfg.m, ld.pw.K, ld.pw.block_size) for ld in base)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def one_pass():
+        for ld in base:
+            mnb.mnb_gemm_i8(ld.x, ld.pw, ws, ld.y)
+    first_ms, _ = time_steps([one_pass], 1, 0, torch)
+    n = max(5, min(steps, int(200.0 / max(first_ms, 1e-3))))
+    ms, _ = time_steps([one_pass], n, 2, torch)
+    tops = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {cfg.name} int8 compute mode: per-linear {ms * 1e3:.1f} us/step ({tops:.1f} TOP/s)")
+    del base, ws
+    torch.cuda.empty_cache()
+    return {"workload": cfg.name, "schedule": "per-linear mnb_gemm_i8 (quantize + int8 matrix-core product)",
+            "launches_per_step": 2 * len(cfg.linears), "steps": n, "ms_per_step": round(ms, 5),
+            "value": round(tops, 2), "unit": "TOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": 5000.0, "unit": "TOP/s",
+                         "frac": round(tops / 5000.0, 4), "note": "int8 dense MFMA peak"}}
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -820,6 +849,8 @@ def main():
         pre = run_workload(pcfg, args.steps, args.warmup, not args.no_per_linear, torch, dev, args.launch_events,
                            floor=True)
         result["prefill"] = leg_record(pcfg, pre, kernel_of(pcfg))
+        if not args.no_int8 and pcfg.dtype == "f16":
+            result["prefill"]["int8_mode"] = run_int8_prefill(pcfg, args.steps, args.warmup, torch, dev)
 
     legs = {}
     for ci in extra:
