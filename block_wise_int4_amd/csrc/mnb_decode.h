@@ -115,6 +115,38 @@ __host__ __device__ __forceinline__ int64_t decode_staged_k(int64_t kg) { return
 constexpr int kGemvMaxLds = 160 * 1024;     // LDS of one CU
 constexpr int kDefaultLds = 64 * 1024;      // above this a launch must opt in
 
+// Relative streaming rates of the persistent decode workgroups, and the
+// split of a launch's work by them. Workgroups are dispatched one per CU in
+// block order (workgroup w is in slot w / 256 of its CU) and round-robin over
+// the XCDs (w % 8). Timestamps of every workgroup of the decode steps gave
+// the same rates on the 0.6B and the 1.7B step: a CU's first workgroup
+// streams fastest, its second at about 0.9 and its third at 0.75 of that
+// rate (the CU issues older waves first), and workgroups on the odd XCDs at
+// 0.935 of the even ones' (measured with equal work per workgroup, then
+// corrected once from the end times the weighted split gave).
+// decode_rate_prefix(v, wgs): the summed rates of workgroups [0, v).
+__host__ __device__ inline double decode_rate_prefix(int64_t v, int64_t wgs) {
+    const double kSlot[3] = {1.0, 0.895, 0.75};
+    const double kOdd = 0.935;
+    const double per8 = 4.0 + 4.0 * kOdd;  // eight consecutive workgroups
+    const bool slots = wgs > 256;          // more than one workgroup per CU
+    const int64_t s = v / 256, j = v % 256, r = j % 8;
+    double sum = 0.0;
+    for (int64_t k = 0; k < s; ++k) sum += (slots ? kSlot[k < 2 ? k : 2] : 1.0) * 32.0 * per8;
+    const double rs = slots ? kSlot[s < 2 ? s : 2] : 1.0;
+    return sum + rs * ((double)(j / 8) * per8 + (double)((r + 1) / 2) + (double)(r / 2) * kOdd);
+}
+
+// First batch of workgroup w when `nbat` batches of one product are split
+// over `wgs` workgroups: by rate when there are at least four batches per
+// workgroup, evenly otherwise (where rounding to whole batches would cost
+// more than the rates gain).
+__host__ __device__ inline int64_t decode_split(int64_t nbat, int64_t w, int64_t wgs) {
+    if (nbat < 4 * wgs) return nbat * w / wgs;
+    if (w >= wgs) return nbat;
+    return (int64_t)((double)nbat * decode_rate_prefix(w, wgs) / decode_rate_prefix(wgs, wgs));
+}
+
 // Kernels whose dynamic LDS may exceed the default must opt in. Each kernel's
 // limit is raised once per device, to the largest size any call can ask
 // for, and never lowered, so concurrent callers cannot undo each other's

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(kD
 void decode_kernel(Problem p, int64_t wgs) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int64_t nbat = p.batch_end;  // batch_begin = 0 for a single problem
-    const int64_t b0 = nbat * blockIdx.x / wgs, b1 = nbat * (blockIdx.x + 1) / wgs;
+    const int64_t b0 = decode_split(nbat, blockIdx.x, wgs), b1 = decode_split(nbat, blockIdx.x + 1, wgs);
     decode_range<T, false>(nullptr, p, 0, b0, b1, smem);
 }
 
@@ -215,7 +215,7 @@ void decode_argmax_kernel(Problem p, int64_t wgs, unsigned long long *slots) {
     __shared__ unsigned long long wave_best[kGemvWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t nbat = p.batch_end;
-    const int64_t b0 = nbat * blockIdx.x / wgs, b1 = nbat * (blockIdx.x + 1) / wgs;
+    const int64_t b0 = decode_split(nbat, blockIdx.x, wgs), b1 = decode_split(nbat, blockIdx.x + 1, wgs);
     uint64_t best = decode_range<T, false, true>(nullptr, p, 0, b0, b1, smem);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
@@ -387,11 +387,13 @@ int64_t gemv_schedule(Problem *entries, int count, GemvWg *table, int max_wgs) {
         cost += (p.batch_end - p.batch_begin) * (p.kg + 1);
     }
     const int64_t wgs = nbat < max_wgs ? nbat : max_wgs;
-    // workgroup w starts at the first batch whose cost prefix reaches w * cost / wgs
+    // workgroup w starts at the first batch whose cost prefix reaches its
+    // share of the cost (shares proportional to the workgroups' rates)
+    const double total_rate = decode_rate_prefix(wgs, wgs);
     int pi = 0;
     int64_t b = 0, prefix = 0;
     for (int64_t w = 0; w <= wgs; ++w) {
-        const int64_t target = cost * w / wgs;
+        const int64_t target = w == wgs ? cost : (int64_t)((double)cost * decode_rate_prefix(w, wgs) / total_rate);
         while (b < nbat && prefix < target) {
             while (b >= entries[pi].batch_end) ++pi;
             prefix += entries[pi].kg + 1;

@@ -544,7 +544,7 @@ __global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(kD
 void decode_i8_kernel(Problem p, int64_t wgs) {
     extern __shared__ __align__(16) uint8_t smem[];
     const int64_t nbat = p.batch_end;
-    const int64_t b0 = nbat * blockIdx.x / wgs, b1 = nbat * (blockIdx.x + 1) / wgs;
+    const int64_t b0 = decode_split(nbat, blockIdx.x, wgs), b1 = decode_split(nbat, blockIdx.x + 1, wgs);
     decode_i8_range<T, false>(nullptr, p, 0, b0, b1, smem);
 }
 
