@@ -238,8 +238,20 @@ __global__ __launch_bounds__(kGemvThreads) void argmax_finish_kernel(const unsig
                                                                      int64_t *index) {
     __shared__ unsigned long long wave_best[kGemvWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // every slot load is issued before any is compared: the slot arrays hold
+    // kGemvMaxWgs slots, so all of them are read, and those past `count`
+    // (left from earlier calls) are dropped afterwards
+    constexpr int kPer = (kGemvMaxWgs + kGemvThreads - 1) / kGemvThreads;
+    static_assert(kPer * kGemvThreads == kGemvMaxWgs, "whole passes over the slots");
+    unsigned long long v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v[i] = slots[threadIdx.x + i * kGemvThreads];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if ((int)threadIdx.x + i * kGemvThreads >= count) v[i] = 0ull;
     unsigned long long b = 0;
-    for (int w = threadIdx.x; w < count; w += kGemvThreads) b = slots[w] > b ? slots[w] : b;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) b = v[i] > b ? v[i] : b;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         const unsigned long long o = __shfl_xor(b, off);

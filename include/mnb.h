@@ -205,8 +205,8 @@ int mnb_gemv_argmax(const void *x, const void *packed, void *y, int64_t *index, 
  * copy until the process ends. Every call on a device shares that device's
  * array: calls that may overlap on one device (different streams) race and
  * must not be issued; calls one after another on one stream are safe. The
- * array needs no clearing: each call writes every slot it reads. Arguments,
- * results and errors otherwise as mnb_gemv_argmax.
+ * array needs no clearing: each call writes every slot whose value it
+ * uses. Arguments, results and errors otherwise as mnb_gemv_argmax.
  */
 int mnb_gemv_argmax_noalloc(const void *x, const void *packed, void *y, int64_t *index,
                             int64_t N, int64_t K, int bits, int block_size, int dtype, void *stream);
