@@ -265,7 +265,7 @@ int mnb_gemv(const void *x, const void *packed, void *y, int64_t N, int64_t K, i
 
 size_t mnb_plan_bytes(int count) {
     if (count < 1 || count > kMaxPlanProblems) return 0;
-    return sizeof(PlanHeader) + sizeof(Problem) * (size_t)count +
+    return sizeof(PlanHeader) + sizeof(Problem) * ((size_t)count + kPlanExtraEntries) +
            sizeof(GemvWg) * (size_t)kGemvMaxWgs * kGemvMaxLaunches;
 }
 
@@ -303,7 +303,7 @@ int plan_grouped(const mnb_problem *problems, int count, int bits, int block_siz
     if (st == MNB_OK) {
         PlanHeader *hdr = static_cast<PlanHeader *>(plan);
         Problem *entries = reinterpret_cast<Problem *>(hdr + 1);
-        GemvWg *tables = reinterpret_cast<GemvWg *>(entries + count);
+        GemvWg *tables = reinterpret_cast<GemvWg *>(entries + count + kPlanExtraEntries);
         memset(hdr, 0, sizeof(PlanHeader));
         hdr->magic = kPlanMagic;
         hdr->version = MNB_ABI_VERSION;
@@ -342,7 +342,11 @@ int plan_grouped(const mnb_problem *problems, int count, int bits, int block_siz
                         st = MNB_ERR_PLAN;
                         break;
                     }
-                    wgs = gemm_xcd_schedule(entries + L.first, L.count, &L.split);
+                    // (the entries after this launch's are free: launches are laid out in order)
+                    int n_out = L.count;
+                    wgs = gemm_xcd_schedule(entries + L.first, L.count, &L.split, &n_out);
+                    out = L.first + n_out;
+                    L.count = n_out;
                 }
                 if ((kind == kKindGemv && v < 2) || kind == kKindGemvI8) {
                     if (decode_tables >= kGemvMaxLaunches) {
@@ -403,7 +407,7 @@ int mnb_gemm_grouped(const void *plan_host, const void *plan_device, void *strea
     const Problem *dev = reinterpret_cast<const Problem *>(static_cast<const PlanHeader *>(plan_device) + 1);
     for (int i = 0; i < hdr->n_launch; ++i) {
         const PlanLaunch &L = hdr->launches[i];
-        if (L.first < 0 || L.count < 1 || L.first + L.count > hdr->count) return MNB_ERR_PLAN;
+        if (L.first < 0 || L.count < 1 || L.first + L.count > hdr->count + kPlanExtraEntries) return MNB_ERR_PLAN;
         hipError_t e;
         if (L.kind == kKindGemm) {
             e = launch_gemm_grouped(dev + L.first, L.count, L.split, L.variant, as_stream(stream));

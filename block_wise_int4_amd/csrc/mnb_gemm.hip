@@ -497,8 +497,8 @@ __device__ __forceinline__ int find_gemm_problem(const Problem *entries, int fir
 }
 
 // Grouped launches: XCD x (blocks b with b % 8 == x) runs its own tile range
-// (whole products, balanced by work on the host, longest K first); blocks
-// past the end of their XCD's range exit at once.
+// (products and runs of a product's tiles, balanced by work on the host,
+// longest K first); blocks past the end of their XCD's range exit at once.
 template <int MF, int NF, int WM, int WN, int MaxBufs>
 __global__ __launch_bounds__(64 * WM *WN) void gemm_grouped_kernel(const Problem *entries, int count,
                                                                    XcdSplit split) {
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(64 * WM *WN) void gemm_grouped_kernel(const Problem
     if (wg >= split.begin[x + 1]) return;
     const int i = find_gemm_problem(entries, split.first[x], split.first[x + 1], wg);
     const Problem p = entries[i];
-    gemm_workgroup<MF, NF, WM, WN, MaxBufs, false>(p, wg - p.wg_begin, lds);
+    gemm_workgroup<MF, NF, WM, WN, MaxBufs, false>(p, wg - p.wg_begin + p.tile_off, lds);
 }
 
 // Split-K: y = float16(part[0] + part[1] + ... + part[S - 1]), the parts
@@ -645,46 +645,88 @@ hipError_t launch_gemm(const Problem &p, int variant, hipStream_t st) {
     return hipGetLastError();
 }
 
-int64_t gemm_xcd_schedule(Problem *entries, int count, XcdSplit *split) {
-    // whole products to XCDs, largest first, each to the least loaded XCD;
-    // a product costs its tiles times (K-tiles + 2): a workgroup's start and
-    // end take about as long as two K-tiles
-    std::vector<int> idx(count), xcd(count);
+int64_t gemm_xcd_schedule(Problem *entries, int count, XcdSplit *split, int *out_count) {
+    // A workgroup costs its K-tiles plus 2: its start and end take about as
+    // long as two K-tiles.
+    auto tile_cost = [&](int i) { return (int64_t)entries[i].kg + 2; };
+    struct Piece {
+        int prod;
+        int64_t t0, t1;  // tiles [t0, t1) of the product
+    };
+    // whole products to XCDs, largest first, each to the least loaded XCD
+    std::vector<int> idx(count);
     for (int i = 0; i < count; ++i) idx[i] = i;
-    auto cost = [&](int i) { return (int64_t)entries[i].tiles_m * entries[i].tiles_n * (entries[i].kg + 2); };
+    auto cost = [&](int i) { return (int64_t)entries[i].tiles_m * entries[i].tiles_n * tile_cost(i); };
     std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return cost(a) > cost(b); });
-    int64_t load[kXcds] = {0};
+    std::vector<Piece> pieces[kXcds];
+    int64_t load[kXcds] = {0}, total = 0;
     for (int i : idx) {
         int best = 0;
         for (int x = 1; x < kXcds; ++x)
             if (load[x] < load[best]) best = x;
-        xcd[i] = best;
+        pieces[best].push_back(Piece{i, 0, (int64_t)entries[i].tiles_m * entries[i].tiles_n});
         load[best] += cost(i);
+        total += cost(i);
     }
-    // entries grouped by XCD; inside a group the products with more K-tiles
+    // Whole products leave the XCDs up to one product apart. Where that is
+    // more than 2% of an XCD's share, move the last tiles of the shortest-K
+    // product of the most loaded XCD to the least loaded one, at most
+    // kXcdMoves times; each move adds one entry. The moved tiles are the
+    // product's last ones (its last output rows), so its other tiles keep
+    // sharing their activation rows in one L2. (Below 2% the moves measured
+    // slower: the XCDs' own speeds differ by about that much, and a moved
+    // run of tiles reads its weights into a second L2.)
+    for (int mv = 0; mv < kXcdMoves; ++mv) {
+        int h = 0, l = 0;
+        for (int x = 1; x < kXcds; ++x) {
+            if (load[x] > load[h]) h = x;
+            if (load[x] < load[l]) l = x;
+        }
+        const int64_t target = (total + kXcds - 1) / kXcds;
+        if (50 * (load[h] - load[l]) <= target) break;
+        const int64_t want = std::min(load[h] - target, target - load[l]);
+        int pick = -1;
+        for (int q = 0; q < (int)pieces[h].size(); ++q) {
+            const Piece &c = pieces[h][q];
+            if (c.t1 - c.t0 >= 2 && (pick < 0 || entries[c.prod].kg <= entries[pieces[h][pick].prod].kg)) pick = q;
+        }
+        if (pick < 0) break;
+        Piece &c = pieces[h][pick];
+        const int64_t tc = tile_cost(c.prod);
+        int64_t n = (want + tc / 2) / tc;
+        if (n > c.t1 - c.t0 - 1) n = c.t1 - c.t0 - 1;
+        if (n <= 0) break;
+        const Piece moved{c.prod, c.t1 - n, c.t1};
+        c.t1 -= n;
+        load[h] -= n * tc;
+        load[l] += n * tc;
+        pieces[l].push_back(moved);
+    }
+    // entries grouped by XCD; inside a group the pieces with more K-tiles
     // come first, so that each XCD ends on short workgroups
     std::vector<Problem> out;
-    out.reserve(count);
+    out.reserve((size_t)count + kXcdMoves);
     int64_t tiles = 0, widest = 0;
     for (int x = 0; x < kXcds; ++x) {
-        std::vector<int> mine;
-        for (int i = 0; i < count; ++i)
-            if (xcd[i] == x) mine.push_back(i);
-        std::stable_sort(mine.begin(), mine.end(), [&](int a, int b) { return entries[a].kg > entries[b].kg; });
+        std::vector<Piece> &mine = pieces[x];
+        std::stable_sort(mine.begin(), mine.end(),
+                         [&](const Piece &a, const Piece &b) { return entries[a.prod].kg > entries[b.prod].kg; });
         split->begin[x] = (int32_t)tiles;
         split->first[x] = (int32_t)out.size();
         const int64_t t0 = tiles;
-        for (int i : mine) {
-            Problem p = entries[i];
+        for (const Piece &c : mine) {
+            Problem p = entries[c.prod];
             p.wg_begin = tiles;
-            tiles += (int64_t)p.tiles_m * p.tiles_n;
+            p.tile_off = (int32_t)c.t0;
+            tiles += c.t1 - c.t0;
             out.push_back(p);
         }
         if (tiles - t0 > widest) widest = tiles - t0;
     }
     split->begin[kXcds] = (int32_t)tiles;
     split->first[kXcds] = (int32_t)out.size();
-    for (int i = 0; i < count; ++i) entries[i] = out[i];
+    for (size_t i = 0; i < out.size(); ++i) entries[i] = out[i];
+    *out_count = (int)out.size();
     return widest * kXcds;
 }
 

@@ -28,6 +28,7 @@ struct Problem {
     int32_t variant;         // kernel variant index (see mnb_gemm.hip / mnb_gemv.hip)
     int32_t tiles_m, tiles_n;
     int32_t ksplit;          // prefill kernel: K parts per output tile (1 = none)
+    int32_t tile_off;        // prefill grouped launches: first output tile of this entry
     float *part;             // with ksplit > 1: float32 partial sums [ksplit][m][n]
 };
 
@@ -36,7 +37,8 @@ enum Kind : int32_t { kKindGemv = 0, kKindGemm = 1, kKindGemvI8 = 2 };
 
 // Prefill launches: the output tiles of XCD x (blocks b with b % 8 == x)
 // are tiles [begin[x], begin[x + 1]) of the launch, and they belong to
-// products [first[x], first[x + 1]) of the launch's entries.
+// entries [first[x], first[x + 1]) of the launch (an entry is a whole
+// product or a run of its tiles, from tile_off on).
 constexpr int kXcdCount = 8;
 struct XcdSplit {
     int32_t begin[kXcdCount + 1];
@@ -65,6 +67,11 @@ constexpr int kGemvMaxLaunches = 3;
 constexpr uint32_t kPlanMagic = 0x4D4E4250u;  // "PBNM"
 constexpr int kMaxPlanLaunches = 16;
 constexpr int kMaxPlanProblems = 65536;
+// Prefill launches may split a product's tiles over two XCDs: each split
+// adds one entry, at most kXcdMoves per launch and 5 prefill launches (one
+// per tile shape) per plan.
+constexpr int kXcdMoves = kXcdCount - 1;
+constexpr int kPlanExtraEntries = 5 * kXcdMoves;
 
 struct PlanHeader {
     uint32_t magic;
@@ -157,7 +164,9 @@ hipError_t launch_gemm(const Problem &p, int variant, hipStream_t st);
 hipError_t launch_gemm_grouped(const Problem *dev_entries, int count, const XcdSplit &split, int variant,
                                hipStream_t st);
 // Host: order and split the problems of one prefill launch across the XCDs
-// (fills wg_begin of each entry); returns the launch's workgroup count.
-int64_t gemm_xcd_schedule(Problem *entries, int count, XcdSplit *split);
+// (fills wg_begin and tile_off of each entry). entries has room for
+// count + kXcdMoves entries; *out_count receives the number written.
+// Returns the launch's workgroup count.
+int64_t gemm_xcd_schedule(Problem *entries, int count, XcdSplit *split, int *out_count);
 
 }  // namespace mnb

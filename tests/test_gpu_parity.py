@@ -172,13 +172,20 @@ def test_grouped_tiles_across_products(band, bs):
         n = int(rng.choice([64, 100, 200, 256, 520, 777]))
         k = int(ks[i % len(ks)])
         specs.append((m, n, k, 1000 + i))
+    _grouped_vs_single(specs, bs)
+
+
+def _grouped_vs_single(specs, bs):
+    """One grouped plan over specs [(m, n, k, seed)], outputs filled with NaN
+    beforehand (so a tile the launch skips shows), against single calls
+    (bitwise) and the oracle (tolerance)."""
     problems, singles, refs = [], [], []
     for m, n, k, seed in specs:
         w, x = synth.random_case(seed, m, n, k, "f16")
         q, s, zp, qw, pz = quantize_oracle(w, bs, np.float16)
         pw = upload_packed(qw, s, pz, n, k, bs)
         xd = torch.from_numpy(x).to(DEV)
-        problems.append((xd, pw, None))
+        problems.append((xd, pw, torch.full((m, n), float("nan"), dtype=torch.float16, device=DEV)))
         singles.append(mnb.mnb_gemm(xd, pw))
         refs.append((x, q, zp, s))
     plan = mnb.mnb_plan_grouped(problems, bs, torch.float16)
@@ -188,6 +195,19 @@ def test_grouped_tiles_across_products(band, bs):
         assert torch.equal(y, ys), (m, n, k)
         ok, err, mx = oracle.within_tolerance(y.cpu().numpy(), oracle.matmul_nbits(x, q, zp, s, bs), 2e-3)
         assert ok, (m, n, k, err, mx)
+
+
+@pytest.mark.parametrize("layers", [1, 3, 12])
+def test_grouped_tiles_moved_between_xcds(layers):
+    """Encoder-shaped products (q/k/v/o, fc1, fc2 of a 768-wide layer at 400
+    rows, block 64) whose whole-product split leaves the XCDs unequal, so
+    that the schedule moves the last tiles of short-K products to other
+    XCDs: every output still written once, bit-equal to single calls."""
+    specs = []
+    for li in range(layers):
+        for j, (n, k) in enumerate([(768, 768)] * 4 + [(3072, 768), (768, 3072)]):
+            specs.append((400, n, k, 5000 + 10 * li + j))
+    _grouped_vs_single(specs, 64)
 
 
 def test_calls_run_on_the_current_stream():
