@@ -8,6 +8,8 @@
 //   write     grid-stride, every thread writes its pieces
 //   read1:2   reads 512 MiB, writes 1 GiB (the embedding gather's mix:
 //             one int8 byte in, one float16 out)
+//   size      "read nt" at the sizes of single decode launches (90, 346 and
+//             997 MB), back to back over rotating windows of the buffer
 // Built by __graft_entry__.build() to workloads/_build/stream_ceiling; by hand:
 //   hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops \
 //       workloads/stream_ceiling.hip -o workloads/_build/stream_ceiling
@@ -108,6 +110,22 @@ int main() {
         const double r4 = time_ms([&] { stream_read_nt<4><<<blocks, 256>>>(d, n, out); }, reps);
         printf("blocks %5d  read nt, contiguous chunks: %6.0f GB/s (2 in flight)  %6.0f GB/s (4 in flight)\n", blocks,
                per2 * blocks * 16.0 / (r2 * 1e-3) / 1e9, per4 * blocks * 16.0 / (r4 * 1e-3) / 1e9);
+    }
+    // Reads the size of one decode launch (the LM head alone, the 0.6B and
+    // the 1.7B steps), back to back, each launch reading the next window of
+    // the buffer so that no launch finds its bytes in the last-level cache.
+    for (size_t mb : {90, 346, 997}) {
+        const size_t wn = mb * 1000000 / 16, windows = n / wn;
+        int r = 0;
+        const int blocks = 768;
+        const size_t per = wn / blocks / 512 * 512;
+        const double ms = time_ms(
+            [&] {
+                stream_read_nt<2><<<blocks, 256>>>(d + (size_t)(r++ % windows) * wn, wn, out);
+            },
+            reps * 4);
+        printf("size %4zu MB  read nt, contiguous chunks, 768 blocks: %6.0f GB/s (%.1f us per launch)\n", mb,
+               per * blocks * 16.0 / (ms * 1e-3) / 1e9, ms * 1e3);
     }
     for (int blocks : {1024, 2048, 4096}) {
         const double r = time_ms([&] { stream_read<<<blocks, 256>>>(d, n, out); }, reps);
