@@ -32,6 +32,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak
 LLC_BYTES = 256e6              # Infinity Cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+MFMA_COUNTERS_FILE = os.path.join(ROOT, "profiles", "mfma_counters.json")
 # sources each measured kernel is built from (counter data is tied to them)
 KERNEL_SOURCES = {
     "decode_grouped_kernel": ("mnb_gemv.hip", "mnb_decode.h", "mnb_device.h", "mnb_layout.h", "mnb_internal.h"),
@@ -64,6 +65,20 @@ def stored_traffic(kernel_key):
     if not rec or rec.get("source_sha") != kernel_source_sha(kernel_key.split(":")[0]):
         return None
     return rec.get("bytes_per_launch")
+
+
+def stored_mfma_counters(kernel_key):
+    """The matrix pipes' busy fraction and the clock measured with rocprofv3
+    counters for this kernel source and workload, or None if absent or taken
+    on a different source."""
+    try:
+        with open(MFMA_COUNTERS_FILE) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != kernel_source_sha(kernel_key.split(":")[0]):
+        return None
+    return rec
 
 
 def record_traffic(fetch_csv, write_csv, probe_mib, workloads, command):
@@ -296,6 +311,7 @@ def summarize_counters(counter_csv, bench_json, timing_json, command, out_path):
             "SQ_VALU_MFMA_BUSY_CYCLES | GRBM_GUI_ACTIVE | busy fraction | clock (GHz) | TFLOP/s |",
             "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
     used = set()
+    records = {}
     for workload, roof, steps, warmup in legs:
         if roof["bound"] != "mfma":
             continue
@@ -314,6 +330,9 @@ def summarize_counters(counter_csv, bench_json, timing_json, command, out_path):
         clock = gui / (t_us * 1e-6) / 1e9 if t_us else float("nan")
         tflops = roof["algorithmic_flops_per_launch"] / (t_us * 1e-6) / 1e12 if t_us else float("nan")
         short = name.split("(")[0].replace("void mnb::", "")
+        records[f"gemm_grouped_kernel:{workload}"] = {
+            "source_sha": kernel_source_sha("gemm_grouped_kernel"), "mfma_busy_fraction": round(busy, 4),
+            "clock_ghz": round(clock, 3), "mfma_flops_per_launch": flops, "command": command}
         text.append(f"| {workload} | `{short}` | {d['SQ_INSTS_MFMA']:.0f} | "
                     f"{flops / roof['algorithmic_flops_per_launch']:.4f} | "
                     f"{d['SQ_INSTS_VALU_MFMA_MOPS_F16'] * 512 / flops:.4f} | {d['SQ_VALU_MFMA_BUSY_CYCLES']:.0f} | "
@@ -324,6 +343,9 @@ def summarize_counters(counter_csv, bench_json, timing_json, command, out_path):
              "ratio. Under the heaviest MFMA load the clock settles lowest."]
     with open(out_path, "w") as f:
         f.write("\n".join(text) + "\n")
+    with open(MFMA_COUNTERS_FILE, "w") as f:
+        json.dump(records, f, indent=1, sort_keys=True)
+        f.write("\n")
     print("\n".join(text))
 
 
@@ -476,6 +498,16 @@ def leg_record(cfg, res, kernel):
                  "launch_us": round(launch_ms * 1e3, 2),
                  "launch_timing": "timed region / steps (one launch per step, back to back)",
                  "algorithmic_bytes_per_launch": res["bytes"]})
+    counters = stored_mfma_counters(f"{kernel}:{cfg.name}") if mb else None
+    if counters:
+        # the same rate against the dense fp16 peak at the clock the counters
+        # measured (256 CUs x 4096 flop per clock), as context for the
+        # 2.4 GHz spec peak that `frac` uses
+        at_clock = 256 * 4096 * counters["clock_ghz"] / 1e3
+        roof["counters"] = {"mfma_busy_fraction": counters["mfma_busy_fraction"],
+                            "clock_ghz": counters["clock_ghz"], "peak_at_clock": round(at_clock, 1),
+                            "frac_at_clock": round(achieved / at_clock, 4),
+                            "source": os.path.relpath(MFMA_COUNTERS_FILE, ROOT)}
     rec = {"workload": cfg.name, "M": cfg.m, "linears": len(cfg.linears), "block_size": cfg.block_size,
            "steps": res["steps"], "warmup": res["warmup"], "ms_per_step": round(res["ms"], 5),
            "first_launch_us": round(res["first_launch_ms"] * 1e3, 2), "schedule": "grouped",

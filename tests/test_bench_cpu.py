@@ -89,3 +89,40 @@ def test_committed_traffic_records_name_their_sources():
         assert kernel in bench.KERNEL_SOURCES
         assert rec["bytes_per_launch"] > 0 and rec["fetch_factor"] > 0 and rec["write_factor"] > 0
         assert len(rec["source_sha"]) == 16 and "rocprofv3 --pmc" in rec["command"]
+
+
+def test_mfma_counters_attach_to_prefill_rooflines(tmp_path, monkeypatch):
+    """A counter record of the current kernel source adds the busy fraction
+    and the rate against the dense peak at the measured clock to an
+    MFMA-bound leg; one taken on other sources, or a decode leg, adds none."""
+    from workloads import configs
+
+    path = tmp_path / "mfma.json"
+    monkeypatch.setattr(bench, "MFMA_COUNTERS_FILE", str(path))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "none.json"))
+    sha = bench.kernel_source_sha("gemm_grouped_kernel")
+    pre = configs.CONFIGS[3]
+    json.dump({f"gemm_grouped_kernel:{pre.name}": {"source_sha": sha, "mfma_busy_fraction": 0.5, "clock_ghz": 2.0}},
+              open(path, "w"))
+    res = {"ms": 1.0, "bytes": 10**9, "flops": 10**12, "replicas": 2, "launches_per_step": 1,
+           "first_launch_ms": 2.0, "steps": 40, "warmup": 20}
+    roof = bench.leg_record(pre, res, "gemm_grouped_kernel")["roofline"]
+    c = roof["counters"]
+    assert c["mfma_busy_fraction"] == 0.5 and c["clock_ghz"] == 2.0
+    assert c["peak_at_clock"] == round(256 * 4096 * 2.0 / 1e3, 1)  # 2097.2 TFLOP/s
+    assert c["frac_at_clock"] == round(roof["achieved"] / c["peak_at_clock"], 4)
+    assert roof["frac"] == round(roof["achieved"] / 2500.0, 4)
+    json.dump({f"gemm_grouped_kernel:{pre.name}": {"source_sha": "0" * 16, "mfma_busy_fraction": 0.5,
+                                                    "clock_ghz": 2.0}}, open(path, "w"))
+    assert "counters" not in bench.leg_record(pre, res, "gemm_grouped_kernel")["roofline"]
+    dec = configs.CONFIGS[1]
+    assert "counters" not in bench.leg_record(dec, res, "decode_grouped_kernel")["roofline"]
+
+
+def test_committed_mfma_counter_records_name_their_sources():
+    data = json.load(open(os.path.join(ROOT, "profiles", "mfma_counters.json")))
+    assert data
+    for key, rec in data.items():
+        assert key.split(":")[0] == "gemm_grouped_kernel"
+        assert 0 < rec["mfma_busy_fraction"] < 1 and 1.0 < rec["clock_ghz"] < 2.5
+        assert len(rec["source_sha"]) == 16 and "rocprofv3 --pmc" in rec["command"]
