@@ -547,11 +547,28 @@ def run_lm_head_argmax(cfg, steps, warmup, torch, dev):
     ws = mnb.argmax_workspace(dev)
     idx = torch.empty(1, dtype=torch.int64, device=dev)
     y = torch.empty(lin.n, dtype=ld.y.dtype, device=dev)
+    # the greedy step's hand-over to the next input embedding: argmax, then
+    # the gather of that token's row (three launches), against the product's
+    # partial results reduced by the gather itself (two launches)
+    from workloads import synth
+    table, scales, _ = synth.embedding_inputs(2, lin.n, lin.k, 1)
+    td, sd = torch.from_numpy(table).to(dev), torch.from_numpy(scales).to(dev)
+    row = torch.empty((1, lin.k), dtype=ld.y.dtype, device=dev)
+    def two_step(p):
+        mnb.mnb_gemv_argmax(x, p, ws, index=idx)
+        mnb.mnb_embed_gather(td, sd, idx, dtype=row.dtype, out=row)
+    def handed_over(p):
+        mnb.mnb_gemv_argmax(x, p, ws, partial=True)
+        mnb.mnb_embed_gather_argmax(td, sd, ws, dtype=row.dtype, out=row, index=idx)
+    kt, _ = time_steps([lambda p=p: two_step(p) for p in pws], steps, warmup, torch)
+    kh, _ = time_steps([lambda p=p: handed_over(p) for p in pws], steps, warmup, torch)
+    del td, sd
     kf, _ = time_steps([lambda p=p: mnb.mnb_gemv_argmax(x, p, ws, index=idx) for p in pws], steps, warmup, torch)
     kg, _ = time_steps([lambda p=p: mnb.mnb_gemv(x, p, y) for p in pws], steps, warmup, torch)
     bf = wbytes + lin.k * a + 8
     bg = wbytes + lin.k * a + lin.n * a
-    log(f"[bench] {cfg.name} LM head {lin.n}x{lin.k}: fused argmax {kf * 1e3:.1f} us, plain {kg * 1e3:.1f} us")
+    log(f"[bench] {cfg.name} LM head {lin.n}x{lin.k}: fused argmax {kf * 1e3:.1f} us, plain {kg * 1e3:.1f} us; "
+        f"argmax then embedding row {kt * 1e3:.1f} us, handed over {kh * 1e3:.1f} us")
     del pws
     torch.cuda.empty_cache()
     return {"shape": [lin.n, lin.k], "replicas": reps,
@@ -559,7 +576,11 @@ def run_lm_head_argmax(cfg, steps, warmup, torch, dev):
                              "algorithmic_bytes": bf, "GBps": round(bf / (kf * 1e-3) / 1e9, 1),
                              "frac_hbm": round(bf / (kf * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
             "plain_gemv": {"us_per_call": round(kg * 1e3, 2), "launches_per_call": 1,
-                           "algorithmic_bytes": bg, "GBps": round(bg / (kg * 1e-3) / 1e9, 1)}}
+                           "algorithmic_bytes": bg, "GBps": round(bg / (kg * 1e-3) / 1e9, 1)},
+            "argmax_to_embedding": {"two_step_us_per_call": round(kt * 1e3, 2), "two_step_launches": 3,
+                                    "handed_over_us_per_call": round(kh * 1e3, 2), "handed_over_launches": 2,
+                                    "embedding": [lin.n, lin.k], "note": "mnb_gemv_argmax + mnb_embed_gather "
+                                    "against mnb_gemv_argmax (partial) + mnb_embed_gather_argmax"}}
 
 
 def run_embed_gather(cfg, steps, warmup, torch, dev, token_counts=(410, 65536)):

@@ -231,7 +231,7 @@ int mnb_embed_gather(const int8_t *table, const float *row_scales, const int64_t
 
 int mnb_gemv_argmax(const void *x, const void *packed, void *y, int64_t *index, void *workspace, int64_t N,
                     int64_t K, int bits, int block_size, int dtype, void *stream) {
-    if (!index || !workspace) return MNB_ERR_NULL;
+    if (!workspace) return MNB_ERR_NULL;
     if ((reinterpret_cast<uintptr_t>(index) & 7) || !aligned16(workspace)) return MNB_ERR_ALIGN;
     Problem p;
     int kind = 0, variant = 0;
@@ -240,6 +240,18 @@ int mnb_gemv_argmax(const void *x, const void *packed, void *y, int64_t *index, 
     if (st) return st;
     p.y = y;
     return hip_status(launch_gemv_argmax(p, variant, workspace, index, as_stream(stream)));
+}
+
+int mnb_embed_gather_argmax(const int8_t *table, const float *row_scales, const void *workspace, int64_t *index,
+                            int64_t V, int64_t H, int dtype, void *out, void *stream) {
+    if (!table || !row_scales || !workspace || !out) return MNB_ERR_NULL;
+    if (dtype != MNB_F16 && dtype != MNB_F32) return MNB_ERR_DTYPE;
+    if (V <= 0 || H <= 0 || H % 16 != 0 || V > MNB_MAX_ROWS) return MNB_ERR_SHAPE;
+    if (!aligned16(table) || !aligned16(out) || !aligned16(workspace) || (reinterpret_cast<uintptr_t>(index) & 7) ||
+        (reinterpret_cast<uintptr_t>(row_scales) & 3))
+        return MNB_ERR_ALIGN;
+    return hip_status(launch_embed_gather_argmax(table, row_scales, workspace, argmax_slot_count(V), index, V, H,
+                                                 dtype, out, as_stream(stream)));
 }
 
 int mnb_gemv_argmax_noalloc(const void *x, const void *packed, void *y, int64_t *index, int64_t N, int64_t K,

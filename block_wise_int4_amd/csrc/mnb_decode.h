@@ -147,6 +147,44 @@ __host__ __device__ inline int64_t decode_split(int64_t nbat, int64_t w, int64_t
     return (int64_t)((double)nbat * decode_rate_prefix(w, wgs) / decode_rate_prefix(wgs, wgs));
 }
 
+// The fused LM-head argmax leaves one 64-bit key per workgroup of its
+// launch (the best of the outputs that workgroup produced; larger key =
+// larger value, equal values = lower index). argmax_reduce_slots: the
+// largest of slots[0, count), computed by all kGemvThreads threads of a
+// workgroup together and returned to every thread. The slot array holds
+// kGemvMaxWgs slots, so all of them are loaded at once and those past
+// `count` (left from earlier calls) are dropped afterwards.
+__device__ __forceinline__ unsigned long long argmax_reduce_slots(const unsigned long long *slots, int count) {
+    __shared__ unsigned long long wave_best[kGemvWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int kPer = (kGemvMaxWgs + kGemvThreads - 1) / kGemvThreads;
+    static_assert(kPer * kGemvThreads == kGemvMaxWgs, "whole passes over the slots");
+    unsigned long long v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v[i] = slots[threadIdx.x + i * kGemvThreads];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        if ((int)threadIdx.x + i * kGemvThreads >= count) v[i] = 0ull;
+    unsigned long long b = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) b = v[i] > b ? v[i] : b;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long o = __shfl_xor(b, off);
+        b = o > b ? o : b;
+    }
+    if (lane == 0) wave_best[wave] = b;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kGemvWaves; ++w) b = wave_best[w] > b ? wave_best[w] : b;
+    return b;
+}
+
+// The output index a key names (-1 for the empty key).
+__device__ __forceinline__ int64_t argmax_key_index(unsigned long long key) {
+    return key == 0 ? -1 : (int64_t)(0xFFFFFFFFu - (uint32_t)key);
+}
+
 // Kernels whose dynamic LDS may exceed the default must opt in. Each kernel's
 // limit is raised once per device, to the largest size any call can ask
 // for, and never lowered, so concurrent callers cannot undo each other's

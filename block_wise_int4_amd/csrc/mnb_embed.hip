@@ -12,7 +12,12 @@
 //    rounded float16 (Boldo and Melquiond, "Emulation of FMA and correctly
 //    rounded sums: proved algorithms using rounding to odd", 2008).
 // Ids outside [0, V) produce rows of zeros.
-#include "mnb_internal.h"
+//
+// After the fused LM-head argmax, the gather can take the argmax's
+// per-workgroup partial results instead of an id: one workgroup reduces
+// them to the index (the finishing launch of the argmax, moved into the
+// consumer) and gathers that row.
+#include "mnb_decode.h"
 
 namespace mnb {
 
@@ -26,6 +31,22 @@ __device__ __forceinline__ float mul_round_odd(float q, float s) {
     uint32_t u = __builtin_bit_cast(uint32_t, p);
     if (e != 0.0f && (u & 1u) == 0u) u += ((e > 0.0f) == (p > 0.0f)) ? 1u : 0xFFFFFFFFu;
     return __builtin_bit_cast(float, u);
+}
+
+// 16 consecutive entries of one row: table bytes raw (zeros for an invalid
+// id) times the row's scale s, written to dst[0, 16).
+template <typename T>
+__device__ __forceinline__ void gather16(u32x4 raw, float s, T *dst) {
+    T v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float q = (float)(int8_t)((raw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+        if constexpr (sizeof(T) == 4) v[i] = q * s;
+        else v[i] = (T)mul_round_odd(q, s);
+    }
+#pragma unroll
+    for (int i = 0; i < (int)(16 * sizeof(T) / 16); ++i)
+        reinterpret_cast<u32x4 *>(dst)[i] = reinterpret_cast<const u32x4 *>(v)[i];
 }
 
 template <typename T>
@@ -44,17 +65,39 @@ __global__ __launch_bounds__(64 * kEmbedWaves) void embed_gather_kernel(const in
     for (int64_t c = (int64_t)lane * 16; c < h; c += 64 * 16) {
         u32x4 raw = {0u, 0u, 0u, 0u};
         if (valid) raw = *reinterpret_cast<const u32x4 *>(src + c);
-        T v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float q = (float)(int8_t)((raw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-            if constexpr (sizeof(T) == 4) v[i] = q * s;
-            else v[i] = (T)mul_round_odd(q, s);
-        }
-#pragma unroll
-        for (int i = 0; i < (int)(16 * sizeof(T) / 16); ++i)
-            reinterpret_cast<u32x4 *>(dst + c)[i] = reinterpret_cast<const u32x4 *>(v)[i];
+        gather16<T>(raw, s, dst + c);
     }
+}
+
+// One workgroup: the argmax index from the product's slots, then its row.
+static_assert(kGemvThreads == 64 * kEmbedWaves, "the slot reduction runs on the gather's workgroup");
+template <typename T>
+__global__ __launch_bounds__(kGemvThreads) void embed_gather_argmax_kernel(
+    const int8_t *__restrict__ table, const float *__restrict__ scales, const unsigned long long *__restrict__ slots,
+    int count, int64_t *__restrict__ index, int64_t vocab, int64_t h, T *__restrict__ out) {
+    const int64_t id = argmax_key_index(argmax_reduce_slots(slots, count));
+    if (index && threadIdx.x == 0) *index = id;
+    const bool valid = id >= 0 && id < vocab;
+    const float s = valid ? scales[id] : 0.0f;
+    const int8_t *src = table + (valid ? id : 0) * h;
+    for (int64_t c = (int64_t)threadIdx.x * 16; c < h; c += kGemvThreads * 16) {
+        u32x4 raw = {0u, 0u, 0u, 0u};
+        if (valid) raw = *reinterpret_cast<const u32x4 *>(src + c);
+        gather16<T>(raw, s, out + c);
+    }
+}
+
+hipError_t launch_embed_gather_argmax(const int8_t *table, const float *scales, const void *slots, int64_t count,
+                                      int64_t *index, int64_t vocab, int64_t h, int dtype, void *out,
+                                      hipStream_t st) {
+    const auto *sl = static_cast<const unsigned long long *>(slots);
+    if (dtype == kF16)
+        embed_gather_argmax_kernel<_Float16><<<1, kGemvThreads, 0, st>>>(table, scales, sl, (int)count, index, vocab,
+                                                                          h, static_cast<_Float16 *>(out));
+    else
+        embed_gather_argmax_kernel<float><<<1, kGemvThreads, 0, st>>>(table, scales, sl, (int)count, index, vocab, h,
+                                                                       static_cast<float *>(out));
+    return hipGetLastError();
 }
 
 hipError_t launch_embed_gather(const int8_t *table, const float *scales, const int64_t *ids, int64_t rows,

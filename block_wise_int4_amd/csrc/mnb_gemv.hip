@@ -236,34 +236,8 @@ void decode_argmax_kernel(Problem p, int64_t wgs, unsigned long long *slots) {
 // key of `count` slots, turned back into its output index.
 __global__ __launch_bounds__(kGemvThreads) void argmax_finish_kernel(const unsigned long long *slots, int count,
                                                                      int64_t *index) {
-    __shared__ unsigned long long wave_best[kGemvWaves];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // every slot load is issued before any is compared: the slot arrays hold
-    // kGemvMaxWgs slots, so all of them are read, and those past `count`
-    // (left from earlier calls) are dropped afterwards
-    constexpr int kPer = (kGemvMaxWgs + kGemvThreads - 1) / kGemvThreads;
-    static_assert(kPer * kGemvThreads == kGemvMaxWgs, "whole passes over the slots");
-    unsigned long long v[kPer];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) v[i] = slots[threadIdx.x + i * kGemvThreads];
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-        if ((int)threadIdx.x + i * kGemvThreads >= count) v[i] = 0ull;
-    unsigned long long b = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) b = v[i] > b ? v[i] : b;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const unsigned long long o = __shfl_xor(b, off);
-        b = o > b ? o : b;
-    }
-    if (lane == 0) wave_best[wave] = b;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-#pragma unroll
-        for (int w = 0; w < kGemvWaves; ++w) b = wave_best[w] > b ? wave_best[w] : b;
-        *index = b == 0 ? -1 : (int64_t)(0xFFFFFFFFu - (uint32_t)b);
-    }
+    const unsigned long long b = argmax_reduce_slots(slots, count);
+    if (threadIdx.x == 0) *index = argmax_key_index(b);
 }
 
 template <typename T>
@@ -470,6 +444,7 @@ hipError_t launch_gemv_argmax(const Problem &p0, int variant, void *workspace, i
         return hipErrorInvalidValue;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!index) return hipSuccess;  // the slots stay for a consumer that reduces them (the embedding gather)
     argmax_finish_kernel<<<1, kGemvThreads, 0, st>>>(slots, (int)wgs, index);
     return hipGetLastError();
 }
@@ -510,8 +485,11 @@ hipError_t argmax_scratch(void **slots, int64_t *n_slots) {
     return hipSuccess;
 }
 
-int64_t gemv_argmax_slots(const Problem &p) {
-    const int64_t batches = (p.rg + kGemvWaves - 1) / kGemvWaves;
+int64_t gemv_argmax_slots(const Problem &p) { return argmax_slot_count(p.n); }
+
+int64_t argmax_slot_count(int64_t n) {
+    const int64_t rg = (n + kTileRows - 1) / kTileRows;
+    const int64_t batches = (rg + kGemvWaves - 1) / kGemvWaves;
     return batches < kGemvMaxWgs ? batches : kGemvMaxWgs;
 }
 

@@ -128,8 +128,15 @@ hipError_t launch_embed_gather(const int8_t *table, const float *scales, const i
                                int64_t vocab, int64_t h, int dtype, void *out, hipStream_t st);
 // Decode product (variants 0 and 1) fused with a greedy argmax of y.
 hipError_t launch_gemv_argmax(const Problem &p, int variant, void *workspace, int64_t *index, hipStream_t st);
-// Workspace slots the argmax launch of p writes (one per workgroup).
+// Workspace slots the argmax launch of p writes (one per workgroup), and
+// the same count for an LM head of n rows.
 int64_t gemv_argmax_slots(const Problem &p);
+int64_t argmax_slot_count(int64_t n);
+// The embedding row of the argmax that a product's slots name (and the
+// index itself, where index is not NULL).
+hipError_t launch_embed_gather_argmax(const int8_t *table, const float *scales, const void *slots, int64_t count,
+                                      int64_t *index, int64_t vocab, int64_t h, int dtype, void *out,
+                                      hipStream_t st);
 // This device's library-held argmax slots (device address and slot count),
 // looked up once per device.
 hipError_t argmax_scratch(void **slots, int64_t *n_slots);

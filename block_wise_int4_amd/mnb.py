@@ -55,6 +55,7 @@ _SIGNATURES = {
     "mnb_gemv_argmax": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
     "mnb_gemv_argmax_noalloc": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _int, _int, _vp]),
     "mnb_embed_gather": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _vp]),
+    "mnb_embed_gather_argmax": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _int, _vp, _vp]),
     "mnb_gemm": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _int, _vp]),
     "mnb_gemm_split_k_workspace_bytes": (_sz, [_i64, _i64, _i64, _int, _int, _int, _int]),
     "mnb_gemm_split_k": (_int, [_vp, _vp, _vp, _vp, _sz, _i64, _i64, _i64, _int, _int, _int, _int, _vp]),
@@ -256,10 +257,12 @@ def argmax_workspace(device):
     return torch.empty(ARGMAX_WORKSPACE_BYTES // 8, dtype=torch.int64, device=device)
 
 
-def mnb_gemv_argmax(x, pw, workspace, y=None, index=None, logits=False):
+def mnb_gemv_argmax(x, pw, workspace, y=None, index=None, logits=False, partial=False):
     """Greedy argmax of y = x @ dequant(W)^T, fused into the decode product.
     Returns the index as a device int64 tensor of one element (and y, when
-    logits=True or y is given)."""
+    logits=True or y is given). With partial=True only the per-workgroup
+    partial results are written to workspace (one launch), for
+    mnb_embed_gather_argmax; then the index is None."""
     _check_x(x, pw)
     if x.numel() != pw.K:
         raise ValueError("mnb_gemv_argmax takes one activation row")
@@ -269,13 +272,16 @@ def mnb_gemv_argmax(x, pw, workspace, y=None, index=None, logits=False):
         y = torch.empty(pw.N, dtype=pw.dtype, device=x.device)
     if y is not None:
         _check_buf(y, "y", pw.dtype, pw.N, x.device)
-    if index is None:
-        index = torch.empty(1, dtype=torch.int64, device=x.device)
-    _check_buf(index, "index", torch.int64, 1, x.device)
+    if partial:
+        index = None
+    else:
+        if index is None:
+            index = torch.empty(1, dtype=torch.int64, device=x.device)
+        _check_buf(index, "index", torch.int64, 1, x.device)
     _check("mnb_gemv_argmax", lib().mnb_gemv_argmax(
-        _dev(x, "x"), _dev(pw.packed, "packed"), None if y is None else _dev(y, "y"), _dev(index, "index"),
-        _dev(workspace, "workspace"), pw.N, pw.K, pw.bits, pw.block_size, dtype_code(pw.dtype),
-        _stream(x.device)))
+        _dev(x, "x"), _dev(pw.packed, "packed"), None if y is None else _dev(y, "y"),
+        None if index is None else _dev(index, "index"), _dev(workspace, "workspace"), pw.N, pw.K, pw.bits,
+        pw.block_size, dtype_code(pw.dtype), _stream(x.device)))
     return (index, y) if y is not None else index
 
 
@@ -319,6 +325,32 @@ def mnb_embed_gather(table, row_scales, ids, dtype=torch.float16, out=None):
         _dev(table, "table"), _dev(row_scales, "row_scales"), _dev(ids, "ids"), T, V, H, dtype_code(out.dtype),
         _dev(out, "out"), _stream(table.device)))
     return out
+
+
+def mnb_embed_gather_argmax(table, row_scales, workspace, dtype=torch.float16, out=None, index=None):
+    """The embedding row (int8 table [V, H] times row_scales [V], rounded once
+    to dtype) of the greedy argmax whose partial results a preceding
+    mnb_gemv_argmax(..., partial=True) on an LM head of V rows left in
+    workspace, on the same stream. Returns (out [1, H], index [1])."""
+    if table.dtype != torch.int8 or table.dim() != 2:
+        raise TypeError("table must be int8 [V, H]")
+    if row_scales.dtype != torch.float32 or row_scales.numel() != table.shape[0]:
+        raise TypeError("row_scales must be float32 [V]")
+    if workspace.numel() * workspace.element_size() < ARGMAX_WORKSPACE_BYTES or workspace.device != table.device:
+        raise ValueError("workspace: the argmax workspace the LM head's partial call wrote")
+    V, H = table.shape
+    if out is None:
+        out = torch.empty((1, H), dtype=dtype, device=table.device)
+    _check_buf(out, "out", out.dtype, H, table.device)
+    if index is None:
+        index = torch.empty(1, dtype=torch.int64, device=table.device)
+    _check_buf(index, "index", torch.int64, 1, table.device)
+    if row_scales.device != table.device:
+        raise ValueError("table and row_scales must be on one device")
+    _check("mnb_embed_gather_argmax", lib().mnb_embed_gather_argmax(
+        _dev(table, "table"), _dev(row_scales, "row_scales"), _dev(workspace, "workspace"), _dev(index, "index"),
+        V, H, dtype_code(out.dtype), _dev(out, "out"), _stream(table.device)))
+    return out, index
 
 
 def mnb_gemm(x, pw, y=None):

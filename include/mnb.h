@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define MNB_ABI_VERSION 1
+#define MNB_ABI_VERSION 2
 
 typedef enum mnb_dtype {
     MNB_F32 = 0, /* float32 activations, scales and outputs */
@@ -187,6 +187,8 @@ int mnb_gemv(const void *x, const void *packed, void *y,
  * which a second launch on the same stream reduces to the index. Calls that
  * run one after another may share it; calls that may overlap (different
  * streams) need workspaces of their own. index must be 8-byte aligned.
+ * index may be NULL: then only the partial results are written (one launch),
+ * for mnb_embed_gather_argmax to reduce.
  */
 #define MNB_ARGMAX_WORKSPACE_BYTES 8192
 int mnb_gemv_argmax(const void *x, const void *packed, void *y, int64_t *index, void *workspace,
@@ -225,6 +227,23 @@ int mnb_gemv_argmax_noalloc(const void *x, const void *packed, void *y, int64_t 
  */
 int mnb_embed_gather(const int8_t *table, const float *row_scales, const int64_t *ids, int64_t T, int64_t V,
                      int64_t H, int dtype, void *out, void *stream);
+
+/*
+ * One greedy decoding step's hand-over from the LM head to the next input
+ * embedding (the token the largest logit names, "Qwen3-ASR-1.7B ONNX",
+ * section "Inference Pipeline", and its int8 row times its embed scale,
+ * "Qwen3-ASR-0.6B ONNX for the browser", section "Building the prompt"):
+ * reduces the partial results that mnb_gemv_argmax left in `workspace`
+ * (called with index NULL and N = V, earlier on the same stream) to the
+ * index of the largest logit, the lowest on ties, writes it to *index
+ * (device int64, 8-byte aligned) unless index is NULL, and writes that
+ * token's embedding to out [H] exactly as mnb_embed_gather with one id.
+ * One launch: the argmax's own reducing launch moves into this one.
+ * table, row_scales, H, dtype and alignment as mnb_embed_gather; workspace
+ * as mnb_gemv_argmax (not modified here).
+ */
+int mnb_embed_gather_argmax(const int8_t *table, const float *row_scales, const void *workspace, int64_t *index,
+                            int64_t V, int64_t H, int dtype, void *out, void *stream);
 
 /*
  * General product for any M >= 1: Y[M][N] = X[M][K] * D^T, X and Y

@@ -72,7 +72,16 @@ static void check_invalid_calls(void) {
     CHECK(mnb_gemm((char *)x + 2, w, y, 4, 64, 128, 4, 32, MNB_F16, NULL) == MNB_ERR_ALIGN);
     CHECK(mnb_gemv(x, w, (char *)y + 8, 64, 128, 4, 32, MNB_F16, NULL) == MNB_ERR_ALIGN);
     CHECK(mnb_gemv(x, w, y, 64, MNB_MAX_K * 2, 4, 32, MNB_F16, NULL) == MNB_ERR_SHAPE);
-    CHECK(mnb_gemv_argmax(x, w, y, NULL, ws, 64, 128, 4, 32, MNB_F16, NULL) == MNB_ERR_NULL);
+    /* index NULL asks for the partial results only: accepted, so this fails on bits */
+    CHECK(mnb_gemv_argmax(x, w, y, NULL, ws, 64, 128, 3, 32, MNB_F16, NULL) == MNB_ERR_BITS);
+    CHECK(mnb_embed_gather_argmax((const int8_t *)w, (const float *)x, NULL, idx, 100, 64, MNB_F16, y, NULL) ==
+          MNB_ERR_NULL);
+    CHECK(mnb_embed_gather_argmax((const int8_t *)w, (const float *)x, ws, NULL, 100, 17, MNB_F16, y, NULL) ==
+          MNB_ERR_SHAPE);
+    CHECK(mnb_embed_gather_argmax((const int8_t *)w, (const float *)x, ws, NULL, 100, 64, 7, y, NULL) ==
+          MNB_ERR_DTYPE);
+    CHECK(mnb_embed_gather_argmax((const int8_t *)w, (const float *)x, (char *)ws + 8, NULL, 100, 64, MNB_F16, y,
+                                  NULL) == MNB_ERR_ALIGN);
     CHECK(mnb_gemv_argmax(x, w, y, idx, NULL, 64, 128, 4, 32, MNB_F16, NULL) == MNB_ERR_NULL);
     CHECK(mnb_gemv_argmax(x, w, y, (int64_t *)((char *)idx + 4), ws, 64, 128, 4, 32, MNB_F16, NULL) ==
           MNB_ERR_ALIGN);

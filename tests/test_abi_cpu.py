@@ -27,7 +27,7 @@ def test_exports_every_declared_function(L):
 
 
 def test_abi_version(L):
-    assert L.mnb_abi_version() == 1
+    assert L.mnb_abi_version() == 2
 
 
 def test_status_strings_cover_every_code(L):
@@ -101,7 +101,8 @@ ODD = ctypes.c_void_p((1 << 20) + 8)
     (lambda L: L.mnb_dequant(FAKE, 64, 65, 4, 32, 1, FAKE2, None), SHAPE),
     (lambda L: L.mnb_quantize_rtn(FAKE, 64, 64, 4, 32, 3, FAKE2, FAKE3, FAKE, None), DTYPE),
     (lambda L: L.mnb_quantize_rtn(FAKE, 64, 64, 5, 32, 1, FAKE2, FAKE3, FAKE, None), BITS),
-    (lambda L: L.mnb_gemv_argmax(FAKE, FAKE2, None, None, FAKE3, 64, 64, 4, 32, 1, None), NULL),
+    # index NULL asks for the partial results only: accepted, so this fails on bits
+    (lambda L: L.mnb_gemv_argmax(FAKE, FAKE2, None, None, FAKE3, 64, 64, 3, 32, 1, None), BITS),
     (lambda L: L.mnb_gemv_argmax(FAKE, FAKE2, None, FAKE3, None, 64, 64, 4, 32, 1, None), NULL),
     (lambda L: L.mnb_gemv_argmax(FAKE, FAKE2, None, ctypes.c_void_p((3 << 20) + 4), FAKE, 64, 64, 4, 32, 1,
                                  None), ALIGN),
@@ -113,6 +114,14 @@ ODD = ctypes.c_void_p((1 << 20) + 8)
     (lambda L: L.mnb_embed_gather(FAKE, FAKE2, FAKE, 4, 100, 64, 5, FAKE3, None), DTYPE),
     (lambda L: L.mnb_embed_gather(FAKE, FAKE2, FAKE, 4, 100, 64, 1, ODD, None), ALIGN),
     (lambda L: L.mnb_embed_gather(FAKE, FAKE2, FAKE, 0, 100, 64, 1, FAKE3, None), MNB_OK),
+    (lambda L: L.mnb_embed_gather_argmax(FAKE, FAKE2, None, FAKE3, 100, 64, 1, FAKE, None), NULL),
+    (lambda L: L.mnb_embed_gather_argmax(FAKE, FAKE2, FAKE3, None, 100, 64, 1, None, None), NULL),
+    (lambda L: L.mnb_embed_gather_argmax(FAKE, FAKE2, FAKE3, None, 100, 40, 1, FAKE, None), SHAPE),
+    (lambda L: L.mnb_embed_gather_argmax(FAKE, FAKE2, FAKE3, None, 0, 64, 1, FAKE, None), SHAPE),
+    (lambda L: L.mnb_embed_gather_argmax(FAKE, FAKE2, FAKE3, None, 100, 64, 5, FAKE, None), DTYPE),
+    (lambda L: L.mnb_embed_gather_argmax(FAKE, FAKE2, FAKE3, ctypes.c_void_p((3 << 20) + 4), 100, 64, 1, FAKE,
+                                         None), ALIGN),
+    (lambda L: L.mnb_embed_gather_argmax(FAKE, FAKE2, ODD, None, 100, 64, 1, FAKE, None), ALIGN),
 ])
 def test_invalid_arguments_are_rejected_before_launch(L, call, status):
     assert call(L) == status

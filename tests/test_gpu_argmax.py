@@ -126,3 +126,56 @@ def test_argmax_graph_replays():
         y = mnb.mnb_gemv(xin, pw)
         torch.cuda.synchronize()
         assert int(idx.item()) == int(np.argmax(y.float().cpu().numpy())), f"replay {seed}"
+
+
+@pytest.mark.parametrize("n,k,bs,dt,hidden", [(151936, 1024, 32, np.float16, 1024), (3000, 1024, 32, np.float16, 64),
+                                              (4099, 512, 64, np.float32, 2048), (17, 128, 32, np.float16, 16),
+                                              (1, 32, 32, np.float32, 32)])
+def test_gather_of_the_argmax_equals_the_two_step_form(n, k, bs, dt, hidden):
+    """The LM head's partial results (one launch) handed to the gather, which
+    reduces them itself: the same index as the two-launch argmax, and the
+    same embedding row as mnb_embed_gather of that index, bit for bit; the
+    index is also the first maximum of the call's own logits."""
+    w, x = synth.random_case(n * 3 + k, 1, n, k, "f16" if dt == np.float16 else "f32")
+    pw, _ = _packed(w, bs, dt)
+    table, scales, _ = synth.embedding_inputs(n + hidden, n, hidden, 1)
+    td, sd = torch.from_numpy(table).to(DEV), torch.from_numpy(scales).to(DEV)
+    tdt = torch.float16 if dt == np.float16 else torch.float32
+    xd = torch.from_numpy(x.reshape(-1)).to(DEV)
+    ws = mnb.argmax_workspace(DEV)
+    idx_ref = mnb.mnb_gemv_argmax(xd, pw, ws)
+    row_ref = mnb.mnb_embed_gather(td, sd, idx_ref, dtype=tdt)
+    y = torch.empty(n, dtype=tdt, device=DEV)
+    none, _ = mnb.mnb_gemv_argmax(xd, pw, ws, y=y, partial=True)
+    assert none is None
+    row, idx = mnb.mnb_embed_gather_argmax(td, sd, ws, dtype=tdt)
+    torch.cuda.synchronize()
+    assert int(idx.item()) == int(idx_ref.item()) == int(np.argmax(y.float().cpu().numpy()))
+    assert torch.equal(row, row_ref)
+
+
+def test_gather_of_the_argmax_tie_and_consecutive_steps():
+    """Planted tie (lowest index wins) and two greedy steps in a row on one
+    workspace, the second with a smaller LM head: each step's row and index
+    come from its own product."""
+    n, k, bs, hidden = 2500, 1024, 32, 128
+    w, x = synth.random_case(777, 1, n, k, "f16")
+    w[1700] = (x[0].astype(np.float32) / np.abs(x[0]).max() * 0.05).astype(np.float32)
+    w[9] = w[1700]
+    pw, _ = _packed(w, bs, np.float16)
+    w2, x2 = synth.random_case(778, 1, 300, k, "f16")
+    pw2, _ = _packed(w2, bs, np.float16)
+    table, scales, _ = synth.embedding_inputs(31, n, hidden, 1)
+    td, sd = torch.from_numpy(table).to(DEV), torch.from_numpy(scales).to(DEV)
+    ws = mnb.argmax_workspace(DEV)
+    mnb.mnb_gemv_argmax(torch.from_numpy(x.reshape(-1)).to(DEV), pw, ws, partial=True)
+    row1, idx1 = mnb.mnb_embed_gather_argmax(td, sd, ws)
+    x2d = torch.from_numpy(x2.reshape(-1)).to(DEV)
+    mnb.mnb_gemv_argmax(x2d, pw2, ws, partial=True)
+    row2, idx2 = mnb.mnb_embed_gather_argmax(td[:300].contiguous(), sd[:300].contiguous(), ws)
+    idx2_ref = mnb.mnb_gemv_argmax(x2d, pw2, mnb.argmax_workspace(DEV))
+    torch.cuda.synchronize()
+    assert int(idx1.item()) == 9
+    assert torch.equal(row1, mnb.mnb_embed_gather(td, sd, idx1))
+    assert int(idx2.item()) == int(idx2_ref.item())
+    assert torch.equal(row2, mnb.mnb_embed_gather(td, sd, idx2))
