@@ -1,7 +1,7 @@
 """The library's host code under AddressSanitizer and UndefinedBehavior-
 Sanitizer (CPU only): every source is rebuilt with both sanitizers on its
 host side (device code is built as usual and never runs), linked with the
-plain-C driver tests/host/abi_host_check.c, and run. The driver exercises
+plain-C check program tests/host/abi_host_check.c, and run. The program exercises
 argument validation of every entry point, packed sizes, and grouped plans
 (written, re-read and corrupted on the host); none of its calls reaches a
 GPU."""
