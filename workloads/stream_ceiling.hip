@@ -9,7 +9,9 @@
 //   read1:2   reads 512 MiB, writes 1 GiB (the embedding gather's mix:
 //             one int8 byte in, one float16 out)
 //   size      "read nt" at the sizes of single decode launches (90, 346 and
-//             997 MB), back to back over rotating windows of the buffer
+//             997 MB), back to back over rotating windows of the buffer,
+//             and at 346 MB with 8 pieces per lane in flight (the decode
+//             kernel's 8 KB per wave)
 // Built by __graft_entry__.build() to workloads/_build/stream_ceiling; by hand:
 //   hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops \
 //       workloads/stream_ceiling.hip -o workloads/_build/stream_ceiling
@@ -125,6 +127,21 @@ int main() {
             },
             reps * 4);
         printf("size %4zu MB  read nt, contiguous chunks, 768 blocks: %6.0f GB/s (%.1f us per launch)\n", mb,
+               per * blocks * 16.0 / (ms * 1e-3) / 1e9, ms * 1e3);
+    }
+    // the decode kernel's depth: 8 pieces (8 KB per wave) in flight, then
+    // all of them used, at the 0.6B step's size
+    {
+        const size_t wn = (size_t)346 * 1000000 / 16, windows = n / wn;
+        int r = 0;
+        const int blocks = 768;
+        const size_t per = wn / blocks / 2048 * 2048;
+        const double ms = time_ms(
+            [&] {
+                stream_read_nt<8><<<blocks, 256>>>(d + (size_t)(r++ % windows) * wn, wn, out);
+            },
+            reps * 4);
+        printf("size  346 MB  read nt, 8 in flight, 768 blocks:         %6.0f GB/s (%.1f us per launch)\n",
                per * blocks * 16.0 / (ms * 1e-3) / 1e9, ms * 1e3);
     }
     for (int blocks : {1024, 2048, 4096}) {
