@@ -179,3 +179,43 @@ def test_gather_of_the_argmax_tie_and_consecutive_steps():
     assert torch.equal(row1, mnb.mnb_embed_gather(td, sd, idx1))
     assert int(idx2.item()) == int(idx2_ref.item())
     assert torch.equal(row2, mnb.mnb_embed_gather(td, sd, idx2))
+
+
+def test_gather_of_the_argmax_graph_replays():
+    """The greedy hand-over (partial argmax, then the gather that reduces it)
+    captured in a HIP graph and replayed with new inputs, with eager calls on
+    the same workspace between replays: every replay's index and row equal
+    the eager two-step form's."""
+    n, k, bs, hidden = 151936, 1024, 32, 1024
+    w, _ = synth.random_case(620, 1, n, k, "f16")
+    pw, _ = _packed(w, bs, np.float16)
+    table, scales, _ = synth.embedding_inputs(41, n, hidden, 1)
+    td, sd = torch.from_numpy(table).to(DEV), torch.from_numpy(scales).to(DEV)
+    ws = mnb.argmax_workspace(DEV)
+    xin = torch.empty(k, dtype=torch.float16, device=DEV)
+    idx = torch.empty(1, dtype=torch.int64, device=DEV)
+    row = torch.empty((1, hidden), dtype=torch.float16, device=DEV)
+    _, x0 = synth.random_case(621, 1, n, k, "f16")
+    xin.copy_(torch.from_numpy(x0.reshape(-1)))
+    mnb.mnb_gemv_argmax(xin, pw, ws, partial=True)
+    mnb.mnb_embed_gather_argmax(td, sd, ws, out=row, index=idx)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(DEV)
+    side.wait_stream(torch.cuda.current_stream(DEV))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        mnb.mnb_gemv_argmax(xin, pw, ws, partial=True)
+        mnb.mnb_embed_gather_argmax(td, sd, ws, out=row, index=idx)
+    torch.cuda.synchronize()
+    for seed in range(4):
+        _, x = synth.random_case(630 + seed, 1, n, k, "f16")
+        xin.copy_(torch.from_numpy(x.reshape(-1)))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_idx, got_row = int(idx.item()), row.clone()
+        ref_idx = mnb.mnb_gemv_argmax(xin, pw, ws)  # eager, on the same workspace
+        ref_row = mnb.mnb_embed_gather(td, sd, ref_idx)
+        torch.cuda.synchronize()
+        assert got_idx == int(ref_idx.item()), f"replay {seed}"
+        assert torch.equal(got_row, ref_row), f"replay {seed}"
