@@ -354,7 +354,12 @@ int plan_grouped(const mnb_problem *problems, int count, int bits, int block_siz
                         st = MNB_ERR_PLAN;
                         break;
                     }
-                    // (the entries after this launch's are free: launches are laid out in order)
+                    // (the entries after this launch's are free: launches are laid out in order;
+                    // the schedule may add up to kXcdMoves of them)
+                    if ((int64_t)out + kXcdMoves > (int64_t)count + kPlanExtraEntries) {
+                        st = MNB_ERR_PLAN;
+                        break;
+                    }
                     int n_out = L.count;
                     wgs = gemm_xcd_schedule(entries + L.first, L.count, &L.split, &n_out);
                     out = L.first + n_out;
