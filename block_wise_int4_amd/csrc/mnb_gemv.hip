@@ -203,6 +203,113 @@ void decode_kernel(Problem p, int64_t wgs) {
     decode_range<T, false>(nullptr, p, 0, b0, b1, smem);
 }
 
+// Single products that fill at most one round of workgroups (every decode
+// linear but the LM head) have too few waves to keep the memory and the
+// ALUs busy: with one wave per row group, a row group of K inputs waits for
+// K / 1024 load groups' round trips and arithmetic in sequence, about 2 us
+// per 1024 inputs. Here the S waves of a workgroup (S = 1, 2 or 4) share
+// one row group: the wave with sub-index s takes load groups s, s + S,
+// s + 2S, ..., with two of them in flight at a time, and keeps each group's
+// per-lane result. The first wave of the row group then adds the results
+// of groups 0, 1, 2, ... in order, which is the exact sequence of float
+// additions decode_range makes for the same row group, so the outputs equal
+// the grouped kernel's bit for bit. With S = 1 each wave owns one row group
+// (four per workgroup), as in decode_kernel, with the next load group in
+// flight during the current one's arithmetic.
+template <typename T, int S>
+__global__ __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(kDecodeOcc)))
+void decode_split_kernel(Problem p) {
+    static_assert(S == 1 || S == 2 || S == 4, "waves per row group");
+    constexpr int kRowGroups = kGemvWaves / S;  // row groups per workgroup
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int wave = uniform_int((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+    const int r = lane & 15, j = lane >> 4;
+    const int rgw = wave / S, sub = wave % S;
+    const uint32_t lane_code_off = (uint32_t)lane * 16u;
+    const int64_t kp = decode_staged_k(p.kg);
+    T *xs = reinterpret_cast<T *>(smem);
+    float *xsum = reinterpret_cast<float *>(smem + kp * sizeof(T));
+    const uint32_t e = (uint32_t)((j / (p.bs / kChunk)) * kTileRows + r);
+    const int64_t ngroups = (p.kg + kTG - 1) / kTG;
+    const int64_t g = (int64_t)blockIdx.x * kRowGroups + rgw;
+    const bool have = g < p.rg;
+    // per-lane results of every load group of the workgroup's row groups
+    // (S > 1): [row group of the workgroup][load group][lane]
+    float *parts = xsum + kp / kChunk + (int64_t)rgw * ngroups * 64;
+
+    // this wave's i-th load group is t = sub + i * S; ring slot i % 2
+    Group<T> ring[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t t = sub + (int64_t)i * S;
+        load_group<T>(p, g, t * kTG, have && t < ngroups, lane_code_off, e, ring[i]);
+    }
+    stage_x<T>(p, xs, xsum);
+
+    float acc = 0.0f;
+    for (int64_t t0 = sub; t0 < ngroups; t0 += 2 * S) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int64_t t = t0 + (int64_t)i * S;
+            if (t < ngroups) {
+                const float gm = group_math<T>(ring[i], xs, xsum, t * kTG, j);
+                if constexpr (S == 1) acc += gm;
+                else parts[t * 64 + lane] = gm;
+            }
+            const int64_t tn = t + 2 * S;
+            load_group<T>(p, g, tn * kTG, have && tn < ngroups, lane_code_off, e, ring[i]);
+        }
+    }
+    if constexpr (S > 1) {
+        __syncthreads();
+        if (sub != 0) return;
+        for (int64_t t = 0; t < ngroups; ++t) acc += parts[t * 64 + lane];
+    }
+    acc += __shfl_xor(acc, 16);
+    acc += __shfl_xor(acc, 32);
+    const int64_t n = g * kTileRows + r;
+    if (j == 0 && n < p.n) static_cast<T *>(p.y)[n] = (T)acc;
+}
+
+// Waves per row group for a single decode product, 0 where the split kernel
+// does not apply (more than one round of workgroups even at S = 1, or the
+// per-group results do not fit next to the staged activations).
+int decode_split_waves(const Problem &p, size_t base_lds, size_t *lds) {
+    const int64_t ngroups = (p.kg + kTG - 1) / kTG;
+    // (three load groups also take four waves: one round trip, one wave idle)
+    for (int s = 4; s >= 1; s /= 2) {
+        if ((s == 4 && ngroups < 3) || (s == 2 && ngroups < 2)) continue;
+        const int64_t wgs = (p.rg * s + kGemvWaves - 1) / kGemvWaves;
+        if (wgs > kGemvMaxWgs) continue;
+        const size_t need = base_lds + (s > 1 ? (size_t)(kGemvWaves / s) * ngroups * 64 * 4 : 0);
+        if (need > (size_t)kGemvMaxLds) continue;
+        *lds = need;
+        return s;
+    }
+    return 0;
+}
+
+template <typename T>
+static hipError_t launch_decode_split(const Problem &p, int s, size_t lds, hipStream_t st) {
+    const unsigned grid = (unsigned)((p.rg * s + kGemvWaves - 1) / kGemvWaves);
+    hipError_t e = hipSuccess;
+    switch (s) {
+    case 4:
+        if ((e = allow_lds<decode_split_kernel<T, 4>>(lds)) != hipSuccess) return e;
+        decode_split_kernel<T, 4><<<grid, kGemvThreads, lds, st>>>(p);
+        break;
+    case 2:
+        if ((e = allow_lds<decode_split_kernel<T, 2>>(lds)) != hipSuccess) return e;
+        decode_split_kernel<T, 2><<<grid, kGemvThreads, lds, st>>>(p);
+        break;
+    default:
+        if ((e = allow_lds<decode_split_kernel<T, 1>>(lds)) != hipSuccess) return e;
+        decode_split_kernel<T, 1><<<grid, kGemvThreads, lds, st>>>(p);
+        break;
+    }
+    return hipGetLastError();
+}
+
 // Argmax workspace: one 8-byte slot per workgroup of the product launch.
 static_assert(kGemvMaxWgs * 8 <= MNB_ARGMAX_WORKSPACE_BYTES, "argmax workspace too small");
 
@@ -416,6 +523,11 @@ hipError_t launch_gemv(const Problem &p0, int dtype, int variant, hipStream_t st
     p.batch_begin = 0;
     p.batch_end = (p.rg + kGemvWaves - 1) / kGemvWaves;
     const int64_t wgs = p.batch_end < kGemvMaxWgs ? p.batch_end : kGemvMaxWgs;
+    size_t split_lds = 0;
+    if (const int sw = decode_split_waves(p, lds, &split_lds)) {  // a product of one round of workgroups
+        return variant == 0 ? launch_decode_split<_Float16>(p, sw, split_lds, st)
+                            : launch_decode_split<float>(p, sw, split_lds, st);
+    }
     if (variant == 0) {
         if ((e = allow_lds<decode_kernel<_Float16>>(lds)) != hipSuccess) return e;
         decode_kernel<_Float16><<<(unsigned)wgs, kGemvThreads, lds, st>>>(p, wgs);

@@ -157,6 +157,34 @@ def test_grouped_plan_matches_single_calls_bitwise(bs):
         assert ok, (err, mx)
 
 
+@pytest.mark.parametrize("dt", [np.float16, np.float32])
+def test_single_decode_split_matches_grouped_bitwise(dt):
+    """Single M = 1 products of one round of workgroups (the split kernel:
+    one, two or four waves share a row group's load groups of 1024 inputs)
+    against the grouped kernel (one wave walks a row group's load groups in
+    order) bit for bit, and against the oracle: K from one to nine load
+    groups with ragged K tails, N that leaves the last workgroup partly or
+    wholly past N, the largest staged K in float32, and shapes on both
+    sides of each switch (768 workgroups of 4 row groups, of 1 row group with
+    four waves each, and past them)."""
+    specs = [(1024, 1024), (1024, 2048), (1024, 3072), (2048, 4096), (100, 5120), (70, 6144), (33, 7168),
+             (16, 2176), (48, 8320), (200, 96), (768 * 64, 256), (769 * 64, 256), (12288, 3072),
+             (12304, 3072)] + ([(40, 32768)] if dt == np.float32 else [])
+    for i, (n, k) in enumerate(specs):
+        w, x = synth.random_case(300 + i, 1, n, k, "f16" if dt == np.float16 else "f32")
+        q, s, zp, qw, pz = quantize_oracle(w, 32, dt)
+        pw = upload_packed(qw, s, pz, n, k, 32)
+        xd = torch.from_numpy(x).to(DEV)
+        single = mnb.mnb_gemv(xd.reshape(-1), pw)
+        plan = mnb.mnb_plan_grouped([(xd, pw, None)], 32, TD[dt])
+        (grouped,) = mnb.mnb_gemm_grouped(plan)
+        torch.cuda.synchronize()
+        assert torch.equal(single.reshape(1, n), grouped.reshape(1, n)), (n, k)
+        ok, err, mx = oracle.within_tolerance(single.cpu().numpy().reshape(1, n),
+                                              oracle.matmul_nbits(x, q, zp, s, 32), TOL[dt])
+        assert ok, (n, k, err, mx)
+
+
 @pytest.mark.parametrize("band,bs", [((65, 208), 32), ((65, 208), 64), ((2, 16), 32), ((17, 64), 64),
                                      ((209, 420), 32)])
 def test_grouped_tiles_across_products(band, bs):
