@@ -12,8 +12,9 @@
 //             997 MB), back to back over rotating windows of the buffer,
 //             and at 346 MB with 8 pieces per lane in flight (the decode
 //             kernel's 8 KB per wave)
-// Built by __graft_entry__.build() to workloads/_build/stream_ceiling; by hand:
-//   hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops \
+// A measurement tool, not part of the library (the library build does not
+// compile it). Build and run it by hand:
+//   mkdir -p workloads/_build && hipcc --offload-arch=gfx950 -O3 -Xclang -target-feature -Xclang -packed-fp32-ops \
 //       workloads/stream_ceiling.hip -o workloads/_build/stream_ceiling
 // then run workloads/_build/stream_ceiling on one MI355X.
 #include <hip/hip_runtime.h>
