@@ -38,12 +38,14 @@ FORMATS = [(True, 32), (True, 64), (True, 128), (False, 128), (False, 256), (Tru
 SHAPES = [(64, 256), (17, 384), (1, 128), (40, 4224), (9, 768), (33, 2560)]
 
 
+def _valid(shapes, formats):
+    """(shape, format) pairs whose K is a whole number of blocks."""
+    return [(*sh, sym, bs) for sh in shapes for sym, bs in formats if sh[-1] % bs == 0]
+
+
 @pytest.mark.parametrize("dt", [np.float16, np.float32])
-@pytest.mark.parametrize("symmetric,bs", FORMATS)
-@pytest.mark.parametrize("n,k", SHAPES)
+@pytest.mark.parametrize("n,k,symmetric,bs", _valid(SHAPES, FORMATS))
 def test_quantize_pack_unpack_dequant_bit_exact(n, k, symmetric, bs, dt):
-    if k % bs:
-        pytest.skip("K not a multiple of the block size")
     w = _weight(n, k, bs, seed=n + k + bs)
     q, s, zp = _oracle(w, bs, dt, symmetric)
     qw, pz = oracle.pack_weight(q, zp)
@@ -68,11 +70,8 @@ def test_quantize_pack_unpack_dequant_bit_exact(n, k, symmetric, bs, dt):
 PRODUCTS = [(1, 3072, 1024), (1, 100, 4224), (2, 64, 512), (62, 1024, 3072), (410, 512, 2048), (1500, 256, 768)]
 
 
-@pytest.mark.parametrize("symmetric,bs", FORMATS)
-@pytest.mark.parametrize("m,n,k", PRODUCTS)
+@pytest.mark.parametrize("m,n,k,symmetric,bs", _valid(PRODUCTS, FORMATS))
 def test_products_within_tolerance(m, n, k, symmetric, bs):
-    if k % bs:
-        pytest.skip("K not a multiple of the block size")
     dt = np.float16
     w, x = synth.random_case(m * 13 + n + k + bs, m, n, k, "f16")
     q, s, zp = _oracle(w, bs, dt, symmetric)
