@@ -56,6 +56,17 @@ int prepare_product(const void *x, const void *packed, const void *y, int64_t m,
     return MNB_OK;
 }
 
+// A single matrix-core product (a call of its own, not a plan): its tile
+// variant and K split by the library's cost model, at most max_split parts
+// or exactly force_split (> 0); sets p's tiles and ksplit and returns the
+// variant. Grouped plans keep the tall tiles of prepare_product.
+int single_gemm(Problem &p, int max_split, int force_split) {
+    const GemmChoice c = gemm_single_choice(p, max_split, force_split);
+    gemm_tiles(p, c.variant, &p.tiles_m, &p.tiles_n);
+    p.ksplit = c.ksplit;
+    return c.variant;
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,7 +140,10 @@ int mnb_gemm(const void *x, const void *packed, void *y, int64_t M, int64_t N, i
     int kind = 0, variant = 0;
     int st = prepare_product(x, packed, y, M, N, K, bits, block_size, dtype, &p, &kind, &variant);
     if (st) return st;
-    if (kind == kKindGemm) return hip_status(launch_gemm(p, variant, as_stream(stream)));
+    if (kind == kKindGemm) {
+        variant = single_gemm(p, 1, 1);
+        return hip_status(launch_gemm(p, variant, as_stream(stream)));
+    }
     return hip_status(launch_gemv(p, dtype, variant, as_stream(stream)));
 }
 
@@ -171,17 +185,7 @@ int mnb_gemm_i8(const void *x, const void *packed, void *y, void *workspace, siz
     return hip_status(launch_gemm_i8(p, dtype, workspace, as_stream(stream)));
 }
 
-namespace {
-// The K split a split-K call uses: 0 asks for the library's choice; the
-// split applies to the matrix-core kernel only (float16, M >= 2) and never
-// exceeds the product's K-tiles.
-int effective_ksplit(const Problem &p, int kind, int variant, int ksplit) {
-    if (kind != kKindGemm) return 1;
-    int s = ksplit == 0 ? gemm_auto_ksplit(p, variant) : ksplit;
-    if (s > p.kg) s = (int)p.kg;
-    return s < 1 ? 1 : s;
-}
-}  // namespace
+
 
 size_t mnb_gemm_split_k_workspace_bytes(int64_t M, int64_t N, int64_t K, int bits, int block_size, int dtype,
                                         int ksplit) {
@@ -192,7 +196,9 @@ size_t mnb_gemm_split_k_workspace_bytes(int64_t M, int64_t N, int64_t K, int bit
     static const uint8_t probe[16] __attribute__((aligned(16))) = {0};
     if (prepare_product(probe, probe, probe, M, N, K, bits, block_size, dtype, &p, &kind, &variant) != MNB_OK)
         return 0;
-    return (size_t)gemm_part_bytes(p, effective_ksplit(p, kind, variant, ksplit));
+    if (kind != kKindGemm) return 0;
+    single_gemm(p, MNB_MAX_KSPLIT, ksplit);
+    return (size_t)gemm_part_bytes(p, p.ksplit);
 }
 
 int mnb_gemm_split_k(const void *x, const void *packed, void *y, void *workspace, size_t workspace_bytes,
@@ -204,7 +210,7 @@ int mnb_gemm_split_k(const void *x, const void *packed, void *y, void *workspace
     int st = prepare_product(x, packed, y, M, N, K, bits, block_size, dtype, &p, &kind, &variant);
     if (st) return st;
     if (kind != kKindGemm) return hip_status(launch_gemv(p, dtype, variant, as_stream(stream)));
-    p.ksplit = effective_ksplit(p, kind, variant, ksplit);
+    variant = single_gemm(p, MNB_MAX_KSPLIT, ksplit);
     if (p.ksplit > 1) {
         const int64_t need = gemm_part_bytes(p, p.ksplit);
         if (!workspace) return MNB_ERR_NULL;

@@ -594,34 +594,68 @@ void gemm_tiles(const Problem &p, int variant, int32_t *tiles_m, int32_t *tiles_
 // Workgroups one CU holds at once, per variant (LDS-bound).
 static int wgs_per_cu(int variant) { return variant <= 2 ? 2 : 1; }
 constexpr int kCus = 256;
-constexpr int kMaxKSplit = 16;
 
-// Choice of the K split, from a cost model fitted to single-product timings
-// on MI355X: a workgroup takes (K-tiles + 2) steps (its start and end cost
-// about two K-tiles), a step takes t0 with the chip lightly loaded and up to
-// 1.6 t0 with every workgroup slot busy, workgroups beyond one round of slots
-// run in further rounds, and a split adds its float32 partial sums (written
-// once, read once) at about 6 TB/s plus about 6 us for the partial-sum
-// epilogue and the second launch (measured: the adding kernel alone takes 3
-// to 4 us). The split with the lowest estimate wins; a larger split must be
-// at least 3% better.
-int gemm_auto_ksplit(const Problem &p, int variant) {
-    const double t0 = variant <= 2 ? 1.2 : 2.0;  // microseconds per K-tile step
-    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+// Estimated time (microseconds) of one product on its own at tile variant
+// v, split S ways, from a cost model fitted to single-product timings on
+// MI355X: a workgroup takes (its K-tiles + 2) steps (its start and end cost
+// about two K-tiles); a step takes t0 with the chip lightly loaded (2.0 us
+// for the tall tiles, 1.2 us for the 64-row one) and (1 + a) t0 with every
+// workgroup slot busy (a = 0.45 tall, 1.1 for the 64-row tile, from the
+// grouped launches, whose slots are all busy), in between in proportion to
+// the slots in use; workgroups beyond one round of slots run in further
+// rounds; and a split adds its float32 partial sums (written once, read
+// once) at about 6 TB/s plus about 6 us for the partial-sum epilogue and the
+// second launch (the adding kernel alone takes 3 to 4 us).
+static double gemm_single_us(const Problem &p, int variant, int64_t s) {
+    const bool small = kVariants[variant].mt <= 64;
+    const double t0 = small ? 1.2 : 2.0, a = small ? 1.1 : 0.45;
+    int32_t tm = 0, tn = 0;
+    gemm_tiles(p, variant, &tm, &tn);
+    const int64_t wgs = (int64_t)tm * tn * s;
     const int64_t slots = (int64_t)kCus * wgs_per_cu(variant);
-    const int64_t top = p.kg < kMaxKSplit ? p.kg : kMaxKSplit;
+    const int64_t rounds = (wgs + slots - 1) / slots;
+    const double fill = wgs < slots ? (double)wgs / (double)slots : 1.0;
+    const int64_t steps = (p.kg + s - 1) / s + 2;
+    double t = (double)rounds * (double)steps * t0 * (1.0 + a * fill);
+    if (s > 1) t += (2.0 * (double)s + 0.5) * (double)p.m * (double)p.n * 4.0 / 6.0e6 + 6.0;
+    return t;
+}
+
+// A single product's tile variant and K split (1 = none) by the model
+// above. The tile is the grouped launches' tall tile for M's row count, or,
+// when M spans more than one 64-row tile, the 64-row tile: its three to
+// four times as many workgroups fill more of the chip when one product
+// runs alone (measured per call at M = 410 and M = 1500: 16-34% faster for
+// every Qwen3-1.7B and Whisper-small linear, split or not). With
+// `max_split` 1 nothing is split; with `force_split` the split is that
+// (capped at the product's K-tiles). A larger split must be 3% better, and
+// so must the 64-row tile.
+GemmChoice gemm_single_choice(const Problem &p, int max_split, int force_split) {
+    const int tall = gemm_variant(p.m);
+    const int cands[2] = {tall, 2};
+    const int nc = p.m > 64 && tall != 2 ? 2 : 1;
+    GemmChoice best{tall, 1};
     double best_t = 0.0;
-    int best = 1;
-    for (int64_t s = 1; s <= top; ++s) {
-        const int64_t wgs = tiles * s;
-        const int64_t rounds = (wgs + slots - 1) / slots;
-        const double fill = wgs < slots ? (double)wgs / (double)slots : 1.0;
-        const int64_t steps = (p.kg + s - 1) / s + 2;
-        double t = (double)rounds * (double)steps * t0 * (1.0 + 0.6 * fill);
-        if (s > 1) t += (2.0 * (double)s + 0.5) * (double)p.m * (double)p.n * 4.0 / 6.0e6 + 6.0;
-        if (s == 1 || t < 0.97 * best_t) {
-            best_t = t;
-            best = (int)s;
+    for (int c = 0; c < nc; ++c) {
+        const int v = cands[c];
+        int64_t lo = 1, hi = max_split < p.kg ? max_split : p.kg;
+        if (force_split > 0) lo = hi = force_split < p.kg ? force_split : p.kg;
+        if (hi < 1) lo = hi = 1;
+        double vt = 0.0;
+        int64_t vs = lo;
+        int32_t tm = 0, tn = 0;
+        gemm_tiles(p, v, &tm, &tn);
+        if ((int64_t)tm * tn * hi > 0x7FFFFFFFLL) continue;  // past a launch's grid
+        for (int64_t s = lo; s <= hi; ++s) {
+            const double t = gemm_single_us(p, v, s);
+            if (s == lo || t < 0.97 * vt) {
+                vt = t;
+                vs = s;
+            }
+        }
+        if (best_t == 0.0 || vt < 0.97 * best_t) {
+            best_t = vt;
+            best = GemmChoice{v, (int)vs};
         }
     }
     return best;

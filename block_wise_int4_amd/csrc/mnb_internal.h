@@ -161,10 +161,14 @@ hipError_t launch_gemv_i8_grouped(const Problem *dev_entries, const GemvWg *dev_
 // MFMA kernel: fp16 with M >= 2.
 int gemm_variant(int64_t m);
 void gemm_tiles(const Problem &p, int variant, int32_t *tiles_m, int32_t *tiles_n);
-// K parts a single product splits into (when a caller workspace allows it):
-// enough to give the chip several workgroups per CU, each part at least two
-// K-tiles long.
-int gemm_auto_ksplit(const Problem &p, int variant);
+// A single product's tile variant and K split (1 = none), from a cost model
+// of one product running alone: at most max_split parts, or exactly
+// force_split (> 0) parts, never more than the product's K-tiles.
+struct GemmChoice {
+    int variant;
+    int ksplit;
+};
+GemmChoice gemm_single_choice(const Problem &p, int max_split, int force_split);
 // Bytes of float32 partial sums a product split into `ksplit` parts needs.
 int64_t gemm_part_bytes(const Problem &p, int ksplit);
 hipError_t launch_gemm(const Problem &p, int variant, hipStream_t st);

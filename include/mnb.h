@@ -252,7 +252,12 @@ int mnb_embed_gather_argmax(const int8_t *table, const float *row_scales, const 
  * rather than the usual int8"). M = 1 runs the decode kernel; float16 with
  * M >= 2 runs the matrix-core (MFMA) kernel that dequantizes weight tiles
  * and feeds fp16 MFMA with float32 accumulation; float32 with M >= 2 runs a
- * vector kernel.
+ * vector kernel. A single matrix-core call picks its output tile from a
+ * cost model of one product running alone: the tall tiles that grouped
+ * plans use, or 64-row tiles when M spans several of them and the tall
+ * tiles would leave much of the GPU idle. The tile does not change the
+ * float32 sum any output element is built from, so the result is the same
+ * either way.
  */
 int mnb_gemm(const void *x, const void *packed, void *y,
              int64_t M, int64_t N, int64_t K, int bits, int block_size, int dtype, void *stream);
@@ -270,9 +275,10 @@ int mnb_gemm(const void *x, const void *packed, void *y,
  * grouped differently. Other calls (M = 1, float32) run exactly as
  * mnb_gemm and ignore the workspace.
  *
- * ksplit: 0 = the library's choice (enough ranges to give every compute
- * unit work, each range at least two tiles long, none when the output
- * tiles already fill the GPU); 1 = no split (one launch, as mnb_gemm);
+ * ksplit: 0 = the library's choice (the split, and the output tile as in
+ * mnb_gemm, with the lowest time in a cost model of one product running
+ * alone; none when the output tiles already fill the GPU); 1 = no split
+ * (one launch, as mnb_gemm);
  * 2..MNB_MAX_KSPLIT = that many ranges, capped at the number of 128-input
  * tiles. Anything else: MNB_ERR_INVALID.
  *
