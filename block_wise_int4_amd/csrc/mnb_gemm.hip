@@ -598,17 +598,19 @@ constexpr int kCus = 256;
 // Estimated time (microseconds) of one product on its own at tile variant
 // v, split S ways, from a cost model fitted to single-product timings on
 // MI355X: a workgroup takes (its K-tiles + 2) steps (its start and end cost
-// about two K-tiles); a step takes t0 with the chip lightly loaded (2.0 us
-// for the tall tiles, 1.2 us for the 64-row one) and (1 + a) t0 with every
-// workgroup slot busy (a = 0.45 tall, 1.1 for the 64-row tile, from the
-// grouped launches, whose slots are all busy), in between in proportion to
-// the slots in use; workgroups beyond one round of slots run in further
-// rounds; and a split adds its float32 partial sums (written once, read
-// once) at about 6 TB/s plus about 6 us for the partial-sum epilogue and the
-// second launch (the adding kernel alone takes 3 to 4 us).
+// about two K-tiles); a step takes t0 with the chip lightly loaded (0.95,
+// 1.05 and 1.2 us for the 16-, 32- and 64-row tiles, 2.0 us for the tall
+// ones) and (1 + a) t0 with every workgroup slot busy (a = 1.0, 1.25, 1.1
+// and 0.45, from the grouped launches, whose slots are all busy), in
+// between in proportion to the slots in use; workgroups beyond one round of
+// slots run in further rounds; and a split adds its float32 partial sums
+// (written once, read once) at about 6 TB/s plus about 6 us for the
+// partial-sum epilogue and the second launch (the adding kernel alone takes
+// 3 to 4 us).
 static double gemm_single_us(const Problem &p, int variant, int64_t s) {
-    const bool small = kVariants[variant].mt <= 64;
-    const double t0 = small ? 1.2 : 2.0, a = small ? 1.1 : 0.45;
+    static const double kT0[kNumVariants] = {0.95, 1.05, 1.2, 2.0, 2.0};
+    static const double kFull[kNumVariants] = {1.0, 1.25, 1.1, 0.45, 0.45};
+    const double t0 = kT0[variant], a = kFull[variant];
     int32_t tm = 0, tn = 0;
     gemm_tiles(p, variant, &tm, &tn);
     const int64_t wgs = (int64_t)tm * tn * s;
@@ -622,18 +624,24 @@ static double gemm_single_us(const Problem &p, int variant, int64_t s) {
 }
 
 // A single product's tile variant and K split (1 = none) by the model
-// above. The tile is the grouped launches' tall tile for M's row count, or,
-// when M spans more than one 64-row tile, the 64-row tile: its three to
-// four times as many workgroups fill more of the chip when one product
-// runs alone (measured per call at M = 410 and M = 1500: 16-34% faster for
-// every Qwen3-1.7B and Whisper-small linear, split or not). With
-// `max_split` 1 nothing is split; with `force_split` the split is that
-// (capped at the product's K-tiles). A larger split must be 3% better, and
-// so must the 64-row tile.
+// above. The candidates are the grouped launches' tile for M's row count
+// and shorter ones whose extra workgroups fill more of the chip when one
+// product runs alone: past 64 rows the 64-row tile (measured per call at
+// M = 410 and M = 1500: 16-34% faster than the tall tiles for every
+// Qwen3-1.7B and Whisper-small linear, split or not), up to 64 rows the
+// 32- and 16-row tiles (at M = 62 the 16-row tile was 15-20% faster than
+// the 64-row one for every Qwen3-0.6B linear). With `max_split` 1 nothing
+// is split; with `force_split` the split is that (capped at the product's
+// K-tiles). A larger split must be 3% better, and so must a shorter tile.
 GemmChoice gemm_single_choice(const Problem &p, int max_split, int force_split) {
     const int tall = gemm_variant(p.m);
-    const int cands[2] = {tall, 2};
-    const int nc = p.m > 64 && tall != 2 ? 2 : 1;
+    int cands[3] = {tall, 2, 2};
+    int nc = 1;
+    if (p.m > 64) {
+        nc = 2;
+    } else {
+        for (int v = tall - 1; v >= 0; --v) cands[nc++] = v;
+    }
     GemmChoice best{tall, 1};
     double best_t = 0.0;
     for (int c = 0; c < nc; ++c) {
